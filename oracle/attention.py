@@ -1,0 +1,202 @@
+"""Attention: FP64 dense reference and the tiled online-softmax recurrence.
+
+Test infrastructure (see ``oracle/__init__``).
+
+``dense_attention`` is the definition softmax(Q K^T * scale) V with its log2
+normalizer, in float64 on the unquantized inputs: the accuracy reference
+(TeleFuser PR #40, "Smooth Attention Kernel Accuracy", measures against dense
+attention; FastVideo PR #2048, "Test Results", reports the output and the
+log2-LSE).
+
+``tiled_attention`` walks the keys in 128-token tiles in the FlashAttention
+order that VC-Attention builds on (summary, "Methodology in Plain English"
+and abstract: an online softmax that keeps a running row max and row sum):
+per tile j, with scores s in log2 units,
+
+    m'   = max(m, max_t s_t)                 running max, once per tile
+    p_t  = 2^(s_t - m')                      FP32 exponential
+    P~   = cast of p to E4M3 (see below)
+    l_j  = tile row sum                      the row sum the recurrence keeps
+    l    = 2^(m - m') l + l_j
+    acc  = 2^(m - m') acc + s_V,j (P~ . R~_j) + l_j mu_V,j
+    m    = m'
+
+and O = acc / l, lse2 = m + log2 l + qmu.  The last term of ``acc`` is the
+rank-one restore of the block's V mean from the tile row sum (VC-Attention
+summary, Key Contribution 1: "restored inside the existing online-softmax
+recurrence using the row sum the kernel already accumulates").
+
+Probability casts (``pcast``):
+
+* ``"e4m3"``: P~ = E4M3(p * 2^8) * 2^-8 and l_j = sum of the FP32 p before
+  the cast.  Reading: the pages do not fix P's scale; 2^8 is a power of two
+  (exact), maps p = 1 to 256 (code 0x78) and keeps p >= 2^-14 normal.
+* ``"expcast"``: ExpCast-FP8 (VC-Attention summary, Key Contribution 2 and
+  Methodology): the E4M3 byte is an affine function of log2 of its value, so
+  the code is formed from the log-domain score by one multiply-add and one
+  integer conversion:  code = rint(8 (s - m') + K0), codes below 8 (the
+  subnormals) become 0 ("maps underflow to zero"), codes above 126 are
+  clipped ("keeps codes in the normal E4M3 range"), and the byte is used as
+  an E4M3 value as is.  With the same 2^8 offset, an exact mapping would be
+  code = 8 log2(p) + 120 - 8 delta(M), delta(M) = log2(1 + M/8) - M/8 over
+  the eight mantissas M; delta ranges over [0, log2(1.5) - 1/2].  The
+  "minimax centring of the one residual error term" is sigma = half that
+  range, K0 = 120 - 8 sigma.  rint rounds half to even.  l_j is the sum of
+  the decoded probabilities (no FP32 p exists on this path).
+* ``"none"``: no cast (P~ = p), for the exactness pins.
+
+Precision (``fp32=True``): the pages fix the exponential and K centring at
+FP32 and the operands at E4M3; every quantity that decides a code is formed
+in float32 with one rounding per operation, in the order below, so a kernel
+that computes in FP32 takes the same decisions.  With scores S (the exact dot
+product of the E4M3 codes, rounded to float32):
+
+    c_j  = f32(f32(s_Q s_K,j) * c)            c = f32(softmax_scale log2 e)
+    s_t  = f32(S_t c_j)                       (only the max uses these)
+    m'   = max(m, max_t s_t)
+    e4m3:    x_t = f32(S_t c_j + f32(8 - m'))      one FMA
+             p8_t = f32(2^x_t),  P~ code = E4M3(p8_t)
+    expcast: t_t = f32(S_t f32(8 c_j) + f32(K0 - 8 m'))
+    accumulation of l and acc: float64.
+
+A one-FMA expression is evaluated in float64 (the product of two float32
+values is exact there) and rounded once to float32; that equals the
+single-rounded FMA except when the float64 sum lands on a float32 midpoint
+(probability about 2^-29 per element).
+
+With ``fp32=False`` everything is float64 and exp2 is exact to float64.
+
+Pinned by tests/test_oracle_attention.py: brute-force dense attention on
+tiny shapes (S in {1, 7, 128, 129, 300}, D in {64, 128}) with no cast; the
+K-centring invariance; the V-mean restore identity (block and sequence mean);
+joint K/V permutation invariance; constant-V and equal-score cases with the
+E4M3 cast; the ExpCast total-variation bound of Proposition 3.1 (3.64% plus
+the underflow tail) and its two-point extremal row.
+"""
+import numpy as np
+
+from . import e4m3
+
+BLOCK = 128
+
+# ExpCast constants (see module docstring)
+DELTA = np.array([np.log2(1.0 + m / 8.0) - m / 8.0 for m in range(8)])
+SIGMA = 0.5 * (DELTA.max() - DELTA.min())          # 0.0424812...
+K0 = 120.0 - 8.0 * SIGMA                          # 119.6601...
+K0_F32 = np.float32(K0)
+#: per-element log2 error bound of ExpCast: half a code step plus sigma
+EXPCAST_LOG2_ERR = SIGMA + 1.0 / 16.0
+#: Proposition 3.1: worst-case TV distance for that per-element bound
+EXPCAST_TV_BOUND = (2.0 ** EXPCAST_LOG2_ERR - 1.0) / (2.0 ** EXPCAST_LOG2_ERR + 1.0)
+
+
+def dense_attention(q, k, v, softmax_scale):
+    """float64 softmax(q k^T * scale) v and log2 sum_t 2^(c q.k_t), c = scale*log2 e.
+
+    q [R, D], k [S, D], v [S, D] (any float dtype, used exactly).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    z = (q @ k.T) * (float(softmax_scale) / np.log(2.0))   # logits in log2 units
+    zmax = z.max(axis=1, keepdims=True)
+    w = np.exp2(z - zmax)
+    den = w.sum(axis=1, keepdims=True)
+    out = (w @ v) / den
+    lse2 = zmax[:, 0] + np.log2(den[:, 0])
+    return out, lse2
+
+
+def expcast_codes(t):
+    """E4M3 codes from ExpCast pre-codes t = 8 (s - m') + K0 (float array)."""
+    code = np.rint(np.asarray(t, dtype=np.float64))
+    code = np.where(code < 8.0, 0.0, np.minimum(code, 126.0))
+    return code.astype(np.uint8)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
+                    v_mean=None, vmean_mode="none", q_off=None, pcast="e4m3",
+                    fp32=True, block=BLOCK, return_trace=False):
+    """One head, R query rows, the recurrence of the module docstring.
+
+    q_hat   [R, D]   query rows (decoded E4M3 codes, or raw values)
+    q_scale [R]      s_Q of each row's block (1 for raw values)
+    k_hat   [nb*block or more, D]  key rows (decoded codes or raw values)
+    k_scale [nb]     s_K per key block
+    v_hat   [nb*block or more, D]  residual V rows (decoded codes or raw)
+    v_scale [nb]     s_V per key block
+    S       number of valid keys; keys >= S are masked
+    c       score constant softmax_scale * log2 e (float32 when fp32)
+    v_mean  [nb, D] (vmean_mode "block") or [D] ("seq") or None ("none")
+    q_off   [R] log2 offset added to lse2 (qmu), or None
+    Returns (O [R, D] float64, lse2 [R] float64) and, with return_trace, a
+    dict of per-tile P codes (e4m3/expcast) and row sums for diagnostics.
+    """
+    q_hat = np.asarray(q_hat, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v_hat = np.asarray(v_hat, dtype=np.float64)
+    R, D = q_hat.shape
+    nb = (S + block - 1) // block
+    rnd = _f32 if fp32 else (lambda x: np.asarray(x, dtype=np.float64))
+    c = float(c)
+    q_scale = np.broadcast_to(np.asarray(q_scale, dtype=np.float64), (R,))
+
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, D))
+    trace = {"codes": [], "ell": []} if return_trace else None
+    for j in range(nb):
+        lo, hi = j * block, min(S, (j + 1) * block)
+        n = hi - lo
+        kb = k_hat[lo:lo + block]
+        vb = v_hat[lo:lo + block]
+        S_raw = rnd(q_hat @ kb[:n].T)                       # [R, n]
+        cj = rnd(rnd(q_scale * float(k_scale[j])) * c)      # [R]
+        s = rnd(S_raw * cj[:, None])
+        m_new = np.maximum(m, s.max(axis=1))
+        if pcast == "expcast":
+            k0 = float(K0_F32) if fp32 else K0
+            bias = rnd(k0 - 8.0 * m_new)
+            t = rnd(S_raw * rnd(8.0 * cj)[:, None] + bias[:, None])
+            codes = expcast_codes(t)
+            p_tilde = e4m3.decode(codes) * 2.0 ** -8
+            ell = p_tilde.sum(axis=1)
+        else:
+            x8 = rnd(S_raw * cj[:, None] + rnd(8.0 - m_new)[:, None])
+            p8 = rnd(np.exp2(x8))
+            if pcast == "e4m3":
+                codes = e4m3.encode(p8)
+                p_tilde = e4m3.decode(codes) * 2.0 ** -8
+            elif pcast == "none":
+                codes = None
+                p_tilde = p8 * 2.0 ** -8
+            else:
+                raise ValueError(pcast)
+            ell = (p8 * 2.0 ** -8).sum(axis=1)
+        alpha = np.exp2(m - m_new)          # 0 on the first tile (m = -inf)
+        l = alpha * l + ell
+        acc = alpha[:, None] * acc + float(v_scale[j]) * (p_tilde @ vb[:n])
+        if vmean_mode == "block":
+            acc += ell[:, None] * np.asarray(v_mean, dtype=np.float64)[j][None, :]
+        m = m_new
+        if return_trace:
+            trace["codes"].append(codes)
+            trace["ell"].append(ell)
+    out = acc / l[:, None]
+    if vmean_mode == "seq":
+        out = out + np.asarray(v_mean, dtype=np.float64)[None, :]
+    lse2 = m + np.log2(l)
+    if q_off is not None:
+        lse2 = lse2 + np.asarray(q_off, dtype=np.float64)
+    if return_trace:
+        return out, lse2, trace
+    return out, lse2
+
+
+def total_variation(p, q) -> np.ndarray:
+    """Row-wise total-variation distance between two normalized rows."""
+    return 0.5 * np.abs(np.asarray(p) - np.asarray(q)).sum(axis=-1)

@@ -1,0 +1,126 @@
+"""The whole hot path for one head, in the pages' order.
+
+Test infrastructure (see ``oracle/__init__``).
+
+1. optional V-Smooth grouping: integer k-means on V, stable label sort,
+   K and V permuted together (``kmeans``);
+2. exact statistics: mu_K over the sequence, mu_V per 128-token block (or
+   over the sequence) (``smoothing``);
+3. per-block E4M3 quantization of Q, of K - mu_K and of the V residual, and
+   qmu = c q.mu_K from the bf16 q (``smoothing``);
+4. the tiled recurrence with the rank-one mean restore and the chosen P cast
+   (``attention``).
+
+Q, O and lse2 stay in the original token order; only K and V are permuted
+(VC-Attention summary, Methodology: permuting keys permutes the columns of
+the probability matrix exactly as the rows of V).
+
+parity unpinned: the end result (O, lse2) of the quantized pipeline is not
+pinned beyond the oracle itself, because the pages print no worked example
+and the captured activations they measure on are not available.  Every step
+above is pinned on its own (see the per-module docstrings); the pipeline
+itself is checked for the direction of the smoothing effect against FP64
+dense attention (tests/test_oracle_pipeline.py).
+"""
+import numpy as np
+
+from . import attention, e4m3, kmeans, smoothing
+
+BLOCK = 128
+
+
+def default_scale(D: int) -> np.float32:
+    return np.float32(1.0 / np.sqrt(np.float64(D)))
+
+
+def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
+                            smooth=True, vmean_mode="block", kmeans_kt=None,
+                            expcast=False, pcast=None, fp32=True):
+    """Run the hot path on one head.
+
+    q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
+    evaluate (default all).  kmeans_kt: (k, iters) or None.  smooth: K
+    centring and V mean removal on/off (off = the unsmoothed baseline).
+    Returns a dict with O, lse2 and every intermediate the GPU path also
+    produces.
+    """
+    q = np.asarray(q, dtype=np.float32)
+    k = np.asarray(k, dtype=np.float32)
+    v = np.asarray(v, dtype=np.float32)
+    S, D = q.shape
+    if rows is None:
+        rows = np.arange(S)
+    rows = np.asarray(rows, dtype=np.int64)
+    if softmax_scale is None:
+        softmax_scale = default_scale(D)
+    c = smoothing.score_constant(softmax_scale)
+    out = {"rows": rows, "c": c}
+
+    if kmeans_kt is not None:
+        labels, perm, kp, vp = kmeans.kmeans_permute_head(k, v, *kmeans_kt)
+        out["labels"], out["perm"] = labels, perm
+    else:
+        kp, vp = k, v
+    out["k_perm"], out["v_perm"] = kp, vp
+
+    if smooth:
+        k_mean = smoothing.k_seq_mean(kp)
+        kc = smoothing.centre(kp, k_mean)
+        if vmean_mode == "block":
+            v_mean = smoothing.v_block_means(vp)
+            vr = smoothing.residual_blocks(vp, v_mean)
+        elif vmean_mode == "seq":
+            v_mean = smoothing.v_seq_mean(vp)
+            vr = smoothing.centre(vp, v_mean)
+        else:
+            v_mean, vr = None, vp
+        q_off = smoothing.q_log2_offset(q[rows], k_mean, c)
+    else:
+        k_mean, kc, v_mean, vr, q_off = None, kp, None, vp, None
+        vmean_mode = "none"
+    out.update(k_mean=k_mean, v_mean=v_mean, vmean_mode=vmean_mode,
+               v_block_means=smoothing.v_block_means(vp) if smooth else None)
+
+    q_codes, q_scale = smoothing.quantize_blocks(q)
+    k_codes, k_scale = smoothing.quantize_blocks(kc)
+    v_codes, v_scale = smoothing.quantize_blocks(vr)
+    out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
+               k_scale=k_scale, v_codes=v_codes, v_scale=v_scale, q_off=q_off)
+
+    if pcast is None:
+        pcast = "expcast" if expcast else "e4m3"
+    o, lse2 = attention.tiled_attention(
+        e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
+        e4m3.decode(k_codes), k_scale, e4m3.decode(v_codes), v_scale, S, c,
+        v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
+        fp32=fp32)
+    out["O"], out["lse2"] = o, lse2
+    return out
+
+
+def sample_rows(S: int, n: int) -> np.ndarray:
+    """n evenly spaced query rows, always with row 0, row S-1 and a row of the
+    last (possibly ragged) block (TeleFuser PR #40 measures on evenly spaced
+    query positions)."""
+    if n >= S:
+        return np.arange(S)
+    r = np.unique(np.linspace(0, S - 1, n).round().astype(np.int64))
+    last_block = ((S - 1) // BLOCK) * BLOCK
+    extra = [0, S - 1, last_block + (S - 1 - last_block) // 2]
+    return np.unique(np.concatenate([r, np.asarray(extra, dtype=np.int64)]))
+
+
+def error_report(o, ref) -> dict:
+    """MSE, cosine, relative L2 and SQNR (dB) of ``o`` against ``ref``, plus
+    max-abs and RMSE (the metrics of TeleFuser PR #40's accuracy table and of
+    FastVideo PR #2048's error table)."""
+    o = np.asarray(o, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    d = o - ref
+    mse = float(np.mean(d * d))
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    cos = float(o @ ref / max(np.linalg.norm(o) * np.linalg.norm(ref), 1e-300))
+    sqnr = float(10.0 * np.log10(max(np.sum(ref * ref), 1e-300) / max(np.sum(d * d), 1e-300)))
+    return {"mse": mse, "cos": cos, "rel_l2": rel, "sqnr_db": sqnr,
+            "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
+            "rmse": float(np.sqrt(mse))}

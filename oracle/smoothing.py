@@ -1,0 +1,130 @@
+"""Exact K/V statistics and the per-block E4M3 quantizers (one head at a time).
+
+Test infrastructure (see ``oracle/__init__``).
+
+Arrays are per head: ``x[S, D]``, float32 arrays that hold bf16 values
+exactly (the inputs are bf16).  Blocks are 128 consecutive tokens; the last
+block of a ragged sequence holds S mod 128 valid tokens.
+
+Sources
+-------
+* K centring: K minus its sequence mean, computed in FP32 before E4M3
+  quantization, is exact for softmax because q . mu_K is the same for every
+  key of a row (TeleFuser PR #40, "Changes", first bullet).
+* "Exact" K/V statistics in one fused reduction (same list, third bullet):
+  the means here are the exact means (float64 sums of the bf16 values,
+  rounded once to float32).
+* V-Smooth block demeaning: each hardware block subtracts its mean and only
+  the residual is quantized (VC-Attention summary, Key Contribution 1 and
+  "Methodology in Plain English").  The sequence-mean variant is TeleFuser's
+  "centralize V, restore its sequence mean after attention".
+* Block quantization scale: one scale per block set by the block's largest
+  entry (VC-Attention abstract: "a block's quantization scale is set by its
+  largest entries").  Reading: scale = amax / 448 over the block's valid
+  tokens and all channels, in FP32; codes = E4M3(x * (448 / amax)) in FP32.
+  A block with amax == 0 uses scale 1 (all codes 0).  448 / amax is clamped
+  to the largest finite float32 so a denormal amax cannot make it infinite.
+
+Pinned by tests/test_oracle_quant.py (amax element -> +-448, reconstruction
+error within half an E4M3 step, padding, exact centring, mean error of the
+dequantized V).
+"""
+import numpy as np
+
+from . import e4m3
+
+BLOCK = 128
+_F32_MAX = np.float32(np.finfo(np.float32).max)
+LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def n_blocks(S: int, block: int = BLOCK) -> int:
+    return (S + block - 1) // block
+
+
+def score_constant(softmax_scale) -> np.float32:
+    """c = softmax_scale * log2(e), in float32: scores are kept in log2 units
+    so the exponential is exp2 (FlashAttention-style online softmax)."""
+    return np.float32(np.float32(softmax_scale) * LOG2E_F32)
+
+
+def exact_mean_f32(x) -> np.ndarray:
+    """Mean over axis 0 of the values in ``x``: float64 sum, float64 divide,
+    rounded once to float32."""
+    x = np.asarray(x, dtype=np.float64)
+    return (x.sum(axis=0) / np.float64(x.shape[0])).astype(np.float32)
+
+
+def k_seq_mean(k) -> np.ndarray:
+    """mu_K[d]: mean of K over all S tokens (float32)."""
+    return exact_mean_f32(k)
+
+
+def v_seq_mean(v) -> np.ndarray:
+    """mu_V^seq[d]: mean of V over all S tokens (float32)."""
+    return exact_mean_f32(v)
+
+
+def v_block_means(v, block: int = BLOCK) -> np.ndarray:
+    """mu_V^blk[j, d]: mean of V over the valid tokens of block j (float32)."""
+    S = v.shape[0]
+    nb = n_blocks(S, block)
+    out = np.empty((nb, v.shape[1]), dtype=np.float32)
+    for j in range(nb):
+        out[j] = exact_mean_f32(v[j * block:min(S, (j + 1) * block)])
+    return out
+
+
+def centre(x, mean) -> np.ndarray:
+    """float32 x - mean (one float32 subtraction per element)."""
+    return (np.asarray(x, dtype=np.float32) - np.asarray(mean, dtype=np.float32)).astype(np.float32)
+
+
+def residual_blocks(v, block_means, block: int = BLOCK) -> np.ndarray:
+    """float32 V - mu_V^blk[block of the token]."""
+    S = v.shape[0]
+    idx = np.arange(S) // block
+    return (np.asarray(v, dtype=np.float32) - block_means[idx]).astype(np.float32)
+
+
+def quantize_blocks(x, block: int = BLOCK):
+    """Per-block E4M3 quantization of a float32 [S, D] array.
+
+    Returns (codes uint8 [nb*block, D], scale float32 [nb]).  Rows past S are
+    padding and get code 0.  Dequantized value = decode(code) * scale.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    S, D = x.shape
+    nb = n_blocks(S, block)
+    codes = np.zeros((nb * block, D), dtype=np.uint8)
+    scale = np.empty(nb, dtype=np.float32)
+    for j in range(nb):
+        xb = x[j * block:min(S, (j + 1) * block)]
+        amax = np.float32(np.max(np.abs(xb)))
+        if amax > 0:
+            s = np.float32(amax / np.float32(448.0))
+            inv = np.float32(np.float32(448.0) / amax)
+            if not np.isfinite(inv):
+                inv = _F32_MAX
+        else:
+            s = np.float32(1.0)
+            inv = np.float32(1.0)
+        scale[j] = s
+        codes[j * block:j * block + xb.shape[0]] = e4m3.encode((xb * inv).astype(np.float32))
+    return codes, scale
+
+
+def dequantize_blocks(codes, scale, S: int, block: int = BLOCK) -> np.ndarray:
+    """float64 [S, D]: decode(code) * scale of the code's block."""
+    idx = np.arange(S) // block
+    return e4m3.decode(codes[:S]) * scale[idx].astype(np.float64)[:, None]
+
+
+def q_log2_offset(q, k_mean, c) -> np.ndarray:
+    """qmu[s] = c * (q_s . mu_K), float64, from the unquantized (bf16) q.
+
+    Adding it to the log2-LSE of the centred logits gives the log2-LSE of the
+    original logits, because centring K shifts every logit of row s by
+    -c * q_s . mu_K (TeleFuser PR #40, Changes, first bullet).
+    """
+    return np.float64(c) * (np.asarray(q, dtype=np.float64) @ np.asarray(k_mean, dtype=np.float64))
