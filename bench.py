@@ -1,0 +1,148 @@
+"""Benchmark of the FP8 smoothed-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload live]
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: (k-means grouping when the workload has it) ->
+exact K/V statistics -> per-block E4M3 quantizers -> FP8 attention.  The
+default workload is the live DiT layer shape S=32626, H=56, D=128, B=1.
+
+Prints ONE JSON line.  ``value`` is whole-step throughput in the metric's
+unit, 4*B*S^2*D*H / step time.  ``roofline`` is the attention kernel alone,
+timed with HIP events on the stream it is launched on, against MI355X's
+dense FP8 MFMA peak.  ``cpu_baseline`` is the NumPy oracle timed on the
+host on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 smoothed-attn TFLOP/s (4·S²·D·H) and % FP8 MFMA peak, S=32626 H=56 D=128"
+FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBS = 8000.0
+
+
+def _cpu_baseline(w, q, k, v, rows_n):
+    """Time the oracle on one head: quantization of that head's full Q/K/V plus
+    the tiled FP8 recurrence for ``rows_n`` evenly spaced query rows over the
+    whole K/V context.  Throughput counted as 4 * rows * S * D flops."""
+    import workloads
+    from oracle import pipeline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    qh, kh, vh = workloads.head_slices(q, k, v, 0, 0)
+    rows = pipeline.sample_rows(w.S, rows_n)
+    t0 = time.perf_counter()
+    pipeline.smoothed_attention_head(qh, kh, vh, rows=rows, kmeans_kt=w.kmeans,
+                                     expcast=w.expcast)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(rows) * w.S * w.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0 of {w.name} (S={w.S}, D={w.D}): full-head statistics and "
+                      f"E4M3 quantizers{' and k-means' if w.kmeans else ''}, then the "
+                      f"tiled recurrence for {len(rows)} query rows over all {w.S} keys; "
+                      f"{dt:.1f} s wall; flops counted 4*rows*S*D"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="live")
+    ap.add_argument("--expcast", type=int, default=None, help="override the workload's ExpCast flag")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over (batch, head) with no exchange, so N GPUs run N "
+              "independent shares - not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_attention_video_smooth_amd as vs
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[args.workload]
+    expcast = w.expcast if args.expcast is None else bool(args.expcast)
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
+    q, k, v = workloads.generate(w, device=dev)
+    plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast)
+    torch.cuda.synchronize(dev)
+
+    for _ in range(args.warmup):
+        plan.run(q, k, v)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # whole-path steps
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan.run(q, k, v)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # attention kernel alone: HIP events on the current stream, which is the
+    # stream the binding launches on
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.attn()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    attn_ms = e0.elapsed_time(e1) / args.steps
+    attn_tflops = w.flops / (attn_ms * 1e-3) / 1e12
+    print(f"[bench] attention kernel: {attn_ms:.3f} ms, {attn_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    value = w.flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}",
+                   "kmeans": list(w.kmeans) if w.kmeans else None, "expcast": expcast,
+                   "smoothing": "K seq-mean centring + V block-mean restore",
+                   "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+                   "attn_ms": round(attn_ms, 4),
+                   "prep_ms": round(ms_step - attn_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = _cpu_baseline(w, q, k, v, args.cpu_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

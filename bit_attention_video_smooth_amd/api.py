@@ -1,0 +1,177 @@
+"""Thin PyTorch binding of libvsmooth: argument marshalling only.
+
+Every function with a ``vs_`` name mirrors the C entry point of the same
+name in include/vsmooth.h: tensors in, device pointers and sizes out, the
+call issued on the current HIP stream, a non-zero status raised as VsError.
+All arithmetic of the hot path runs in the library's HIP kernels.
+
+``Plan`` preallocates every buffer of one problem size and chains the four
+calls in the method's order (grouping, statistics, quantizers, attention);
+``attention`` is the one-shot convenience wrapper around it.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _abi
+from ._abi import (VS_EXPCAST, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+                   VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
+
+__all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
+           "vs_fp8_attn_fwd", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
+           "vs_version", "Plan", "attention"]
+
+_VMEAN = {"none": VS_VMEAN_NONE, "block": VS_VMEAN_BLOCK, "seq": VS_VMEAN_SEQ}
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libvsmooth takes device tensors")
+            return t.device
+    raise ValueError("no tensor given")
+
+
+def vs_version():
+    return load().vs_version().decode()
+
+
+def vs_smooth_stats_workspace_bytes(B, S, H, D):
+    n = ctypes.c_size_t(0)
+    check(load().vs_smooth_stats_workspace_bytes(B, S, H, D, ctypes.byref(n)),
+          "vs_smooth_stats_workspace_bytes")
+    return n.value
+
+
+def vs_smooth_stats(k, v, shape, layout, k_mean, v_block_mean, v_seq_mean, ws):
+    B, S, H, D = shape
+    dev = _dev(k, v)
+    check(load().vs_smooth_stats(_p(k), _p(v), B, S, H, D, layout, _p(k_mean),
+                                 _p(v_block_mean), _p(v_seq_mean), _p(ws),
+                                 ws.numel() * ws.element_size() if ws is not None else 0,
+                                 _stream(dev)), "vs_smooth_stats")
+
+
+def vs_quantize_residual(q, k, v, kv_layout, shape, softmax_scale, k_mean, v_mean, vmean_mode,
+                         q8, q_scale, k8, k_scale, v8, v_scale, q_mu):
+    B, S, H, D = shape
+    dev = _dev(q, k, v)
+    check(load().vs_quantize_residual(_p(q), _p(k), _p(v), kv_layout, B, S, H, D,
+                                      float(softmax_scale), _p(k_mean), _p(v_mean), vmean_mode,
+                                      _p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v8),
+                                      _p(v_scale), _p(q_mu), _stream(dev)),
+          "vs_quantize_residual")
+
+
+def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, shape,
+                    softmax_scale, flags, out, lse2):
+    B, S, H, D = shape
+    dev = _dev(q8, k8, v8)
+    check(load().vs_fp8_attn_fwd(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v8), _p(v_scale),
+                                 _p(v_mean), vmean_mode, _p(q_mu), B, S, H, D,
+                                 float(softmax_scale), int(flags), _p(out), _p(lse2),
+                                 _stream(dev)), "vs_fp8_attn_fwd")
+
+
+def vs_kmeans_workspace_bytes(B, S, H, D, k_clusters):
+    n = ctypes.c_size_t(0)
+    check(load().vs_kmeans_workspace_bytes(B, S, H, D, k_clusters, ctypes.byref(n)),
+          "vs_kmeans_workspace_bytes")
+    return n.value
+
+
+def vs_kmeans_permute(k, v, shape, k_clusters, iters, labels, perm, k_perm, v_perm, ws):
+    B, S, H, D = shape
+    dev = _dev(k, v)
+    check(load().vs_kmeans_permute(_p(k), _p(v), B, S, H, D, k_clusters, iters, _p(labels),
+                                   _p(perm), _p(k_perm), _p(v_perm), _p(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(dev)), "vs_kmeans_permute")
+
+
+class Plan:
+    """All buffers of one problem, allocated once; ``run`` launches the path.
+
+    shape (B, S, H, D); smooth: K centring + V mean removal; vmean: "block"
+    or "seq" (ignored when smooth is False); kmeans: (k, iters) or None;
+    expcast: ExpCast-FP8 P cast.
+    """
+
+    def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
+                 kmeans=None, expcast=False):
+        B, S, H, D = shape
+        self.shape = tuple(int(x) for x in shape)
+        self.device = torch.device(device)
+        self.softmax_scale = float(softmax_scale) if softmax_scale else 1.0 / math.sqrt(D)
+        self.smooth = smooth
+        self.vmean_mode = _VMEAN[vmean] if smooth else VS_VMEAN_NONE
+        self.kmeans = kmeans
+        self.flags = VS_EXPCAST if expcast else 0
+        nb = (S + 127) // 128
+        dev = self.device
+        f32, u8, i32 = torch.float32, torch.uint8, torch.int32
+        e = lambda *s, dtype=f32: torch.empty(*s, dtype=dtype, device=dev)  # noqa: E731
+        self.q8, self.k8 = e(B, H, nb * 128, D, dtype=u8), e(B, H, nb * 128, D, dtype=u8)
+        self.v8 = e(B, H, nb, D, 128, dtype=u8)
+        self.q_scale, self.k_scale, self.v_scale = e(B, H, nb), e(B, H, nb), e(B, H, nb)
+        self.out, self.lse2 = e(B, S, H, D), e(B, H, S)
+        self.k_mean = self.q_mu = self.v_mean = self.stats_ws = None
+        if smooth:
+            self.k_mean = e(B, H, D)
+            self.q_mu = e(B, H, S)
+            self.v_mean = e(B, H, nb, D) if self.vmean_mode == VS_VMEAN_BLOCK else e(B, H, D)
+            self.stats_ws = e(vs_smooth_stats_workspace_bytes(B, S, H, D), dtype=u8)
+        self.labels = self.perm = self.k_perm = self.v_perm = self.km_ws = None
+        if kmeans is not None:
+            kc, _ = kmeans
+            self.labels, self.perm = e(B, H, S, dtype=i32), e(B, H, S, dtype=i32)
+            self.k_perm = e(B, H, S, D, dtype=torch.bfloat16)
+            self.v_perm = e(B, H, S, D, dtype=torch.bfloat16)
+            self.km_ws = e(vs_kmeans_workspace_bytes(B, S, H, D, kc), dtype=u8)
+
+    def run(self, q, k, v):
+        """Launch the whole path on the current stream; returns (out, lse2)."""
+        shape = self.shape
+        if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
+            raise ValueError(f"expected q, k, v of shape {shape}")
+        for t in (q, k, v):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != self.device:
+                raise ValueError("q, k, v must be contiguous bf16 tensors on the plan's device")
+        layout = VS_LAYOUT_BSHD
+        kk, vv = k, v
+        if self.kmeans is not None:
+            kc, iters = self.kmeans
+            vs_kmeans_permute(k, v, shape, kc, iters, self.labels, self.perm, self.k_perm,
+                              self.v_perm, self.km_ws)
+            kk, vv, layout = self.k_perm, self.v_perm, VS_LAYOUT_BHSD
+        if self.smooth:
+            blk = self.v_mean if self.vmean_mode == VS_VMEAN_BLOCK else None
+            seq = self.v_mean if self.vmean_mode == VS_VMEAN_SEQ else None
+            vs_smooth_stats(kk, vv, shape, layout, self.k_mean, blk, seq, self.stats_ws)
+        vs_quantize_residual(q, kk, vv, layout, shape, self.softmax_scale, self.k_mean,
+                             self.v_mean, self.vmean_mode, self.q8, self.q_scale, self.k8,
+                             self.k_scale, self.v8, self.v_scale, self.q_mu)
+        self.attn()
+        return self.out, self.lse2
+
+    def attn(self):
+        """The attention call alone, on the buffers the last ``run`` filled."""
+        vs_fp8_attn_fwd(self.q8, self.q_scale, self.k8, self.k_scale, self.v8, self.v_scale,
+                        self.v_mean, self.vmean_mode, self.q_mu, self.shape, self.softmax_scale,
+                        self.flags, self.out, self.lse2)
+
+
+def attention(q, k, v, **kw):
+    """One-shot: build a Plan for q's shape and run it; returns (out, lse2)."""
+    plan = Plan(tuple(q.shape), q.device, **kw)
+    return plan.run(q, k, v)

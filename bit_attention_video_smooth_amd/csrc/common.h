@@ -1,0 +1,67 @@
+// Internal helpers shared by the libvsmooth HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "vsmooth.h"
+
+namespace vs {
+
+constexpr int kBlock = 128;            // tokens per quantization block / KV tile
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
+
+inline int n_blocks(int S) { return (S + kBlock - 1) / kBlock; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Status of the most recent launch on this thread.
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Element offset of (b, s, h, d=0) in a [B,S,H,D] or [B,H,S,D] tensor.
+__device__ __forceinline__ size_t token_offset(int layout, int b, int s, int h,
+                                               int S, int H, int D) {
+  return layout == VS_LAYOUT_BSHD
+             ? ((static_cast<size_t>(b) * S + s) * H + h) * D
+             : ((static_cast<size_t>(b) * H + h) * S + s) * D;
+}
+
+// Two float32 values -> two E4M3 bytes written into byte lanes [2*hi, 2*hi+1]
+// of `old` (hardware conversion: round to nearest even; inputs must already
+// lie in [-448, 448]).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HI));
+}
+
+__device__ __forceinline__ float clamp448(float x) {
+  return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
+}
+
+// Wave-wide (64 lanes) reductions through DPP/ds_swizzle-based shuffles.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+}  // namespace vs

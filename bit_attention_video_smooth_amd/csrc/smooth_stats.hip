@@ -1,0 +1,161 @@
+// vs_smooth_stats: exact K/V statistics in one pass over K and V.
+//
+// TeleFuser PR #40 ("Changes") fuses exact K/V statistics into a single
+// reduction, centres K by its sequence mean in FP32 and centres V; the
+// VC-Attention summary (Key Contribution 1) subtracts each hardware block's
+// V mean.  Both means come out of the same pass here:
+//
+//   stage 1, grid (nb, H, B): one workgroup per 128-token block sums K and V
+//     over its valid tokens in float64 (a bf16 value has 8 significant bits,
+//     so these sums are exact), writes the block mean of V and keeps the two
+//     block sums in the workspace.
+//   stage 2, grid (H, B): sums the nb block sums in a fixed order and writes
+//     the sequence means.  Fixed orders make the result deterministic.
+//
+// HBM-bound: K and V are read once (4 bytes per element pair); the float64
+// adds are far below the FP64 vector rate.
+#include "common.h"
+
+namespace vs {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void stats_block_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int layout,
+    int S, int H, int nb, float* __restrict__ v_block_mean,
+    double* __restrict__ ws_k, double* __restrict__ ws_v) {
+  constexpr int CH = D / 8;           // 16-byte chunks per token row
+  constexpr int ROWS = 256 / CH;      // token lanes per workgroup
+  constexpr int TPT = kBlock / ROWS;  // tokens per thread
+  __shared__ double red[ROWS][D];
+
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int c = threadIdx.x % CH, r = threadIdx.x / CH;
+  double sk[8], sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.0;
+
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int tok = j * kBlock + r + ROWS * i;
+    if (tok < S) {
+      const size_t off = token_offset(layout, b, tok, h, S, H, D) + 8 * c;
+      const uint4 kk = *reinterpret_cast<const uint4*>(k + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>(v + off);
+      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[2 * e] += static_cast<double>(bf16_to_f32(kw[e] & 0xFFFFu));
+        sk[2 * e + 1] += static_cast<double>(bf16_to_f32(kw[e] >> 16));
+        sv[2 * e] += static_cast<double>(bf16_to_f32(vw[e] & 0xFFFFu));
+        sv[2 * e + 1] += static_cast<double>(bf16_to_f32(vw[e] >> 16));
+      }
+    }
+  }
+
+  const int n = min(kBlock, S - j * kBlock);
+  const size_t out = ((static_cast<size_t>(b) * H + h) * nb + j) * D;
+  // K block sums
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r][8 * c + e] = sk[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+    for (int rr = 0; rr < ROWS; ++rr) s += red[rr][threadIdx.x];
+    ws_k[out + threadIdx.x] = s;
+  }
+  __syncthreads();
+  // V block sums and block means
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r][8 * c + e] = sv[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+    for (int rr = 0; rr < ROWS; ++rr) s += red[rr][threadIdx.x];
+    ws_v[out + threadIdx.x] = s;
+    if (v_block_mean) v_block_mean[out + threadIdx.x] = static_cast<float>(s / static_cast<double>(n));
+  }
+}
+
+// One workgroup per (b, h): G = 1024 / D groups of D threads each sum a
+// strided subset of the block sums, then group 0 adds the G partials in order.
+template <int D>
+__global__ __launch_bounds__(1024) void stats_seq_kernel(
+    const double* __restrict__ ws_k, const double* __restrict__ ws_v, int S,
+    int H, int nb, float* __restrict__ k_mean, float* __restrict__ v_seq_mean) {
+  constexpr int G = 1024 / D;
+  __shared__ double part[2][G][D];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d = threadIdx.x % D, g = threadIdx.x / D;
+  const size_t base = (static_cast<size_t>(b) * H + h) * nb * D;
+  double sk = 0.0, sv = 0.0;
+  for (int j = g; j < nb; j += G) {
+    sk += ws_k[base + static_cast<size_t>(j) * D + d];
+    sv += ws_v[base + static_cast<size_t>(j) * D + d];
+  }
+  part[0][g][d] = sk;
+  part[1][g][d] = sv;
+  __syncthreads();
+  if (g == 0) {
+    double tk = 0.0, tv = 0.0;
+    for (int gg = 0; gg < G; ++gg) {
+      tk += part[0][gg][d];
+      tv += part[1][gg][d];
+    }
+    const size_t o = (static_cast<size_t>(b) * H + h) * D + d;
+    if (k_mean) k_mean[o] = static_cast<float>(tk / static_cast<double>(S));
+    if (v_seq_mean) v_seq_mean[o] = static_cast<float>(tv / static_cast<double>(S));
+  }
+}
+
+size_t ws_bytes_needed(int B, int S, int H, int D) {
+  return 2 * static_cast<size_t>(B) * H * n_blocks(S) * D * sizeof(double);
+}
+
+}  // namespace
+}  // namespace vs
+
+extern "C" int vs_smooth_stats_workspace_bytes(int B, int S, int H, int D, size_t* bytes) {
+  if (!bytes || B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
+  *bytes = vs::ws_bytes_needed(B, S, H, D);
+  return VS_OK;
+}
+
+extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
+                               int D, int layout, float* k_mean, float* v_block_mean,
+                               float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
+  using namespace vs;
+  if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
+  if (layout != VS_LAYOUT_BSHD && layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0 || H == 0) return VS_OK;
+  if (!k_mean && !v_block_mean && !v_seq_mean) return VS_ERR_INVALID_ARG;
+  if (!k || !v) return VS_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || (k_mean && !aligned16(k_mean)) ||
+      (v_block_mean && !aligned16(v_block_mean)) || (v_seq_mean && !aligned16(v_seq_mean)))
+    return VS_ERR_UNSUPPORTED;
+  const size_t need = ws_bytes_needed(B, S, H, D);
+  if (!ws || ws_bytes < need) return VS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return VS_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
+
+  const int nb = n_blocks(S);
+  double* ws_k = static_cast<double*>(ws);
+  double* ws_v = ws_k + static_cast<size_t>(B) * H * nb * D;
+  hipStream_t st = as_stream(stream);
+  const dim3 g1(nb, H, B), g2(H, B);
+  if (D == 128) {
+    hipLaunchKernelGGL(stats_block_kernel<128>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
+                       v_block_mean, ws_k, ws_v);
+    hipLaunchKernelGGL(stats_seq_kernel<128>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
+                       k_mean, v_seq_mean);
+  } else {
+    hipLaunchKernelGGL(stats_block_kernel<64>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
+                       v_block_mean, ws_k, ws_v);
+    hipLaunchKernelGGL(stats_seq_kernel<64>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
+                       k_mean, v_seq_mean);
+  }
+  return launch_status();
+}

@@ -1,0 +1,194 @@
+/*
+ * vsmooth.h -- C ABI of libvsmooth, FP8 (E4M3) FlashAttention-style forward
+ * with attention-equivalent K/V smoothing, for AMD CDNA4 (gfx950).
+ *
+ * The method (sources cited per entry point):
+ *   - K is centred by its per-head sequence mean in FP32 before E4M3
+ *     quantization; softmax does not change (TeleFuser PR #40, "Changes").
+ *   - V tokens may be grouped by k-means and K and V permuted together; the
+ *     output does not change (VC-Attention summary, Key Contribution 1 and
+ *     "Methodology in Plain English").
+ *   - each 128-token block subtracts its V mean and quantizes the residual;
+ *     the mean is restored inside the online-softmax recurrence as a
+ *     rank-one term from the tile row sum (same sources).
+ *   - the probability tile can be written as E4M3 straight from the
+ *     log-domain score with one FMA (ExpCast-FP8, VC-Attention summary, Key
+ *     Contribution 2).
+ *   - output O and the log2 softmax normalizer (FastVideo PR #2048, "Test
+ *     Results": output plus log2-LSE); inputs [B, S, H, D] (TeleFuser PR #40,
+ *     "Smooth Attention Kernel Accuracy": live shape (1, 32626, 56, 128)).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps device memory; scratch space is
+ *     passed in as a workspace whose size a *_workspace_bytes query returns.
+ *   - bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream), stateless, and safe to call from several host
+ *     threads on different streams.  Calls that share output or workspace
+ *     buffers must be ordered by the caller.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is launched and the outputs are left untouched.
+ *     B, S or H equal to 0 is an empty problem: VS_OK, nothing launched.
+ *   - Pointers must be 16-byte aligned (VS_ERR_UNSUPPORTED otherwise).
+ *   - D must be 64 or 128 (VS_ERR_UNSUPPORTED otherwise).
+ *   - Blocks are 128 consecutive tokens; nb = ceil(S / 128) and
+ *     S_pad = 128 * nb.  The last block of a ragged sequence holds S mod 128
+ *     valid tokens; its padding rows are encoded as 0 and masked.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef VSMOOTH_H
+#define VSMOOTH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define VS_OK               0
+#define VS_ERR_INVALID_ARG  1   /* null pointer, negative size, bad mode   */
+#define VS_ERR_UNSUPPORTED  2   /* D not in {64,128}, k > 256, misaligned   */
+#define VS_ERR_WORKSPACE    3   /* workspace missing or too small           */
+#define VS_ERR_HIP          4   /* a HIP launch or runtime call failed      */
+
+/* token layouts of bf16 K / V inputs */
+#define VS_LAYOUT_BSHD 0        /* [B, S, H, D], D contiguous                */
+#define VS_LAYOUT_BHSD 1        /* [B, H, S, D], D contiguous                */
+
+/* V mean modes */
+#define VS_VMEAN_NONE  0        /* V quantized as is, nothing restored       */
+#define VS_VMEAN_BLOCK 1        /* per-128-block mean, restored per tile     */
+#define VS_VMEAN_SEQ   2        /* one sequence mean, restored at the end    */
+
+/* vs_fp8_attn_fwd flags */
+#define VS_EXPCAST 1u           /* ExpCast-FP8 probability cast              */
+
+/* Human-readable name of a return code (static string, never NULL). */
+const char* vs_status_string(int status);
+
+/* Library version string, "major.minor.patch". */
+const char* vs_version(void);
+
+/*
+ * vs_smooth_stats -- exact K/V statistics in one pass over K and V.
+ * Source: TeleFuser PR #40, "Changes" (fuse exact K/V statistics into one
+ * reduction; centre K in FP32; centre V and restore its mean) and
+ * VC-Attention summary, Key Contribution 1 (per-block V mean).
+ *
+ *   k, v          bf16 [B,S,H,D] (layout VS_LAYOUT_BSHD) or [B,H,S,D]
+ *                 (VS_LAYOUT_BHSD), e.g. the permuted K', V'.
+ *   k_mean        out f32 [B,H,D]: mean of K over the S tokens, or NULL.
+ *   v_block_mean  out f32 [B,H,nb,D]: mean of V over each block's valid
+ *                 tokens, or NULL.
+ *   v_seq_mean    out f32 [B,H,D]: mean of V over the S tokens, or NULL.
+ *   ws, ws_bytes  workspace of at least vs_smooth_stats_workspace_bytes().
+ * Means are exact: float64 sums of the bf16 values, one float64 division,
+ * one rounding to float32.  At least one output must be non-NULL.
+ */
+int vs_smooth_stats_workspace_bytes(int B, int S, int H, int D, size_t* bytes);
+int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
+                    int D, int layout, float* k_mean, float* v_block_mean,
+                    float* v_seq_mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * vs_quantize_residual -- per-128-token-block E4M3 quantizers for Q, centred
+ * K and residual V.  Source: TeleFuser PR #40, "Changes" (centre K in FP32
+ * before E4M3; Q unchanged) and VC-Attention summary, Key Contribution 1
+ * (each hardware block subtracts its mean and quantizes only the residual);
+ * scale set by the block's largest entry (VC-Attention abstract).
+ *
+ *   q             bf16 [B,S,H,D] (always BSHD).
+ *   k, v          bf16 in `kv_layout` (VS_LAYOUT_BSHD or VS_LAYOUT_BHSD).
+ *   softmax_scale the attention scale (1/sqrt(D) is the usual value); used
+ *                 for q_mu only.
+ *   k_mean        f32 [B,H,D] from vs_smooth_stats, or NULL: no K centring.
+ *   v_mean        f32 [B,H,nb,D] (VS_VMEAN_BLOCK) or [B,H,D] (VS_VMEAN_SEQ),
+ *                 or NULL with VS_VMEAN_NONE.
+ *   q8, k8        out u8 [B,H,S_pad,D]: E4M3 codes, row per token.
+ *   v8            out u8 [B,H,nb,D,128]: E4M3 codes of the residual, per
+ *                 block one row of 128 tokens per channel.  Within a block
+ *                 the token of row position p (0..127) is
+ *                   t(p) = 64*(p/64) + 32*((p%32)/16) + 8*((p%16)/4)
+ *                          + 4*((p%64)/32) + p%4
+ *                 (the order the attention kernel's FP8 MFMA consumes).
+ *   q_scale, k_scale, v_scale  out f32 [B,H,nb]: dequantization scales.
+ *   q_mu          out f32 [B,H,S]: c * (q . k_mean) with c = softmax_scale *
+ *                 log2(e), from the bf16 q; required iff k_mean != NULL.
+ * Per block: x = float32 input (minus the mean, one float32 subtraction),
+ * amax = max |x| over the valid tokens and D channels, scale = amax / 448,
+ * code = E4M3(x * (448 / amax)) round-to-nearest-even, saturating at 448
+ * (448 / amax clamped to FLT_MAX); amax == 0 gives scale 1 and codes 0.
+ */
+int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, int kv_layout, int B, int S, int H,
+                         int D, float softmax_scale, const float* k_mean,
+                         const float* v_mean, int vmean_mode, uint8_t* q8,
+                         float* q_scale, uint8_t* k8, float* k_scale,
+                         uint8_t* v8, float* v_scale, float* q_mu,
+                         void* stream);
+
+/*
+ * vs_fp8_attn_fwd -- FP8 attention forward with the in-recurrence V-mean
+ * restore.  Source: VC-Attention summary, Key Contributions 1-2 and
+ * "Methodology in Plain English"; abstract (low-bit matrix cores for QK^T
+ * and PV, FP32 softmax between them); FastVideo PR #2048, "Test Results"
+ * (output and log2-LSE).
+ *
+ *   q8, q_scale, k8, k_scale, v8, v_scale  from vs_quantize_residual.
+ *   v_mean        the same mean buffer given to vs_quantize_residual
+ *                 ([B,H,nb,D] for VS_VMEAN_BLOCK, [B,H,D] for VS_VMEAN_SEQ),
+ *                 NULL with VS_VMEAN_NONE.
+ *   q_mu          f32 [B,H,S] or NULL (then 0).
+ *   flags         0 or VS_EXPCAST.
+ *   out           out f32 [B,S,H,D]: attention output in the caller's
+ *                 query order.
+ *   lse2          out f32 [B,H,S]: log2 sum_t 2^(c * score_t) of the
+ *                 (uncentred) logits: m + log2(l) + q_mu.
+ * Non-causal full attention; keys past S are masked.  Per 128-key tile:
+ * running max m' once per tile; P = E4M3(2^(s - m' + 8)) from an FP32
+ * exp2 (l sums the FP32 p), or with VS_EXPCAST the code
+ * rint(8 (s - m') + K0), K0 = 120 - 4 (log2(1.5) - 1/2), codes < 8 -> 0
+ * (l sums the decoded codes); O accumulates s_V * P.R~ + l_tile * mu_block.
+ */
+int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                    const float* k_scale, const uint8_t* v8,
+                    const float* v_scale, const float* v_mean, int vmean_mode,
+                    const float* q_mu, int B, int S, int H, int D,
+                    float softmax_scale, unsigned flags, float* out,
+                    float* lse2, void* stream);
+
+/*
+ * vs_kmeans_permute -- V-Smooth grouping: integer k-means over each head's V
+ * tokens, stable sort of the labels, K and V gathered by the permutation.
+ * Source: VC-Attention summary, Key Contribution 1 and "Methodology in
+ * Plain English" (lightweight online k-means on V; keys and values permuted
+ * together by the sorted labels; attention unchanged).
+ *
+ *   k, v          bf16 [B,S,H,D] (BSHD).
+ *   k_clusters    1..256;  iters >= 1 Lloyd passes.
+ *   labels        out i32 [B,H,S]: cluster of each token (last assignment).
+ *   perm          out i32 [B,H,S]: perm[i] = source token of position i,
+ *                 ascending label, original order within a label.
+ *   k_perm, v_perm out bf16 [B,H,S,D] (BHSD): K[perm], V[perm] per head.
+ *   ws, ws_bytes  workspace of at least vs_kmeans_workspace_bytes().
+ * Integer definition (bit-exact on any implementation): codes =
+ * rint(V * 2^-e) with 2^e the smallest power of two such that
+ * max|V| <= 127 * 2^e (per head); init centroid j = codes of token
+ * floor(j*S/k); assign argmin_j |c_j|^2 - 2 v.c_j (ties: lowest j);
+ * update c_j = round-half-away(sum/count), empty clusters keep theirs.
+ */
+int vs_kmeans_workspace_bytes(int B, int S, int H, int D, int k_clusters,
+                              size_t* bytes);
+int vs_kmeans_permute(const uint16_t* k, const uint16_t* v, int B, int S,
+                      int H, int D, int k_clusters, int iters, int32_t* labels,
+                      int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSMOOTH_H */

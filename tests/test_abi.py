@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/vsmooth.h declares, and rejects bad arguments on the host before
+anything would be launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsmooth.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_attention_video_smooth_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from bit_attention_video_smooth_amd import build
+        build.build()
+    return _abi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = _declared()
+    for n in ["vs_smooth_stats", "vs_kmeans_permute", "vs_quantize_residual", "vs_fp8_attn_fwd"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from bit_attention_video_smooth_amd import _abi
+    for n in _declared():
+        assert hasattr(lib, n), n
+        assert n in _abi.PROTOTYPES, n
+
+
+def test_status_and_version(lib):
+    assert lib.vs_version().decode().count(".") == 2
+    for s in range(5):
+        assert lib.vs_status_string(s).decode().startswith("VS_")
+    assert b"unknown" in lib.vs_status_string(99)
+
+
+def test_workspace_queries(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.vs_smooth_stats_workspace_bytes(1, 32626, 56, 128, ctypes.byref(n)) == 0
+    assert n.value == 2 * 56 * 255 * 128 * 8
+    assert lib.vs_kmeans_workspace_bytes(1, 32760, 40, 128, 16, ctypes.byref(n)) == 0
+    assert n.value >= 40 * 32760 * 128            # the int8 codes
+    assert lib.vs_kmeans_workspace_bytes(1, 100, 1, 128, 257, ctypes.byref(n)) == 2
+    assert lib.vs_kmeans_workspace_bytes(1, 100, 1, 96, 16, ctypes.byref(n)) == 2
+    assert lib.vs_smooth_stats_workspace_bytes(1, 100, 1, 128, None) == 1
+
+
+def test_attn_argument_errors(lib):
+    f = lib.vs_fp8_attn_fwd
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+    args = lambda **kw: [kw.get("q8", fake), fake, fake, fake, fake, fake,  # noqa: E731
+                         kw.get("vm", None), kw.get("mode", 0), None, kw.get("B", 1),
+                         kw.get("S", 256), 1, kw.get("D", 128), kw.get("scale", 0.1),
+                         kw.get("flags", 0), fake, fake, None]
+    assert f(*args(D=96)) == 2
+    assert f(*args(q8=None)) == 1
+    assert f(*args(B=-1)) == 1
+    assert f(*args(mode=1)) == 1                      # block mean without a buffer
+    assert f(*args(mode=7, vm=fake)) == 1
+    assert f(*args(flags=4)) == 1
+    assert f(*args(scale=0.0)) == 1
+    assert f(*args(q8=ctypes.c_void_p(0x1004))) == 2  # misaligned
+    assert f(*args(S=0)) == 0                         # empty problem
+    assert f(*args(S=0, D=96)) == 2
+
+
+def test_quant_stats_kmeans_argument_errors(lib):
+    fake = ctypes.c_void_p(0x1000)
+    q = lib.vs_quantize_residual
+    base = [fake, fake, fake, 0, 1, 300, 2, 128, 0.1, None, None, 0,
+            fake, fake, fake, fake, fake, fake, None, None]
+    bad = list(base); bad[3] = 5
+    assert q(*bad) == 1                                # bad layout
+    bad = list(base); bad[9] = fake
+    assert q(*bad) == 1                                # k_mean without q_mu
+    bad = list(base); bad[11] = 1
+    assert q(*bad) == 1                                # vmean block without buffer
+    bad = list(base); bad[7] = 32
+    assert q(*bad) == 2
+    s = lib.vs_smooth_stats
+    assert s(fake, fake, 1, 300, 2, 128, 0, None, None, None, fake, 1 << 30, None) == 1
+    assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, fake, 16, None) == 3
+    assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, None, 1 << 30, None) == 3
+    k = lib.vs_kmeans_permute
+    assert k(fake, fake, 1, 300, 2, 128, 16, 0, fake, fake, fake, fake, fake, 1 << 30, None) == 1
+    assert k(fake, fake, 1, 300, 2, 128, 300, 2, fake, fake, fake, fake, fake, 1 << 30, None) == 2
+    assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, fake, fake, 64, None) == 3

@@ -1,0 +1,142 @@
+"""GPU parity of every libvsmooth call against the CPU oracle, on sizes the
+oracle finishes in seconds (several tiles plus ragged tails).
+
+Bars: statistics, scales, E4M3 codes, k-means labels and the permutation
+bit-exact; O within max-abs 2e-3 and relative L2 5e-3, log2-LSE within 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import e4m3, pipeline
+from gpu_util import (check_attn, check_intermediates, dev, oracle_head, plan_head,
+                      run_plan)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(S, n=256):
+    return pipeline.sample_rows(S, n)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_stats_codes_and_attention(name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v)
+    rows = _rows(w.S)
+    for h in range(w.H):
+        print(f"[{name}] head {h}", flush=True)
+        ref = oracle_head(q, k, v, 0, h, rows)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, w.S, label=f"{name} h{h}")
+        np.testing.assert_allclose(got["q_mu"][rows], ref["q_off"], rtol=1e-5, atol=1e-5)
+        check_attn(got["O"], got["lse2"], ref, label=f"{name} h{h}")
+
+
+@pytest.mark.parametrize("smooth,vmean,expcast", [
+    (False, "block", False), (True, "seq", False), (True, "block", True),
+    (False, "block", True), (True, "seq", True)])
+def test_attention_modes(smooth, vmean, expcast):
+    w = workloads.WORKLOADS["mid"]
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, smooth=smooth, vmean=vmean, expcast=expcast)
+    rows = _rows(w.S, 128)
+    for h in (0, 3, 7):
+        ref = oracle_head(q, k, v, 0, h, rows, smooth=smooth, vmean_mode=vmean, expcast=expcast)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, w.S, label=f"h{h}")
+        check_attn(got["O"], got["lse2"], ref, label=f"smooth={smooth} vmean={vmean} "
+                                                     f"expcast={expcast} h{h}")
+
+
+@pytest.mark.parametrize("S", [1, 7, 128, 129, 300])
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_and_tiny_shapes(S, D):
+    w = workloads.Workload("rag", 2, S, 3, D, 100 + S + D, "offsets",
+                           extra=dict(k_off=2.0, k_off_shared=False, v_off=1.0,
+                                      out_frac=0.01, out_mult=10.0))
+    q, k, v = workloads.generate(w)
+    for expcast in (False, True):
+        plan = run_plan(q, k, v, expcast=expcast)
+        rows = np.arange(S)
+        for b in range(2):
+            for h in range(3):
+                ref = oracle_head(q, k, v, b, h, rows, expcast=expcast)
+                got = plan_head(plan, b, h, rows)
+                check_intermediates(got, ref, S, label=f"S{S} D{D} b{b} h{h}")
+                check_attn(got["O"], got["lse2"], ref, label=f"S{S} D{D} b{b} h{h} ec{expcast}")
+
+
+@pytest.mark.parametrize("D,S,kc,iters", [(128, 3000, 16, 4), (64, 2500, 32, 3),
+                                          (128, 700, 200, 2)])
+def test_kmeans_permute_and_grouped_attention(D, S, kc, iters):
+    w = workloads.Workload("g", 1, S, 3, D, 7 + kc, "mixture", kmeans=(kc, iters),
+                           extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, kmeans=(kc, iters))
+    rows = _rows(S, 128)
+    for h in range(3):
+        ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=(kc, iters))
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, S, label=f"kmeans h{h}")
+        kb = k[0, :, h, :].view(torch.int16).numpy()
+        vb = v[0, :, h, :].view(torch.int16).numpy()
+        np.testing.assert_array_equal(got["k_perm"], kb[ref["perm"]])
+        np.testing.assert_array_equal(got["v_perm"], vb[ref["perm"]])
+        check_attn(got["O"], got["lse2"], ref, label=f"kmeans D{D} h{h}")
+
+
+def test_e4m3_conversion_at_rounding_boundaries():
+    """A block whose amax is 448 has scale 1, so the codes are the E4M3
+    rounding of the bf16 values themselves: every midpoint between
+    neighbouring codes (ties to even), both neighbours of it, and values
+    beyond the subnormal range, through all three quantizers."""
+    pos = e4m3.DECODE[:0x7F]
+    mids = 0.5 * (pos[1:] + pos[:-1])
+    vals = np.concatenate([pos, mids, -mids, -pos, np.nextafter(mids.astype(np.float32), np.inf),
+                           np.nextafter(mids.astype(np.float32), -np.inf)]).astype(np.float32)
+    # keep what bf16 holds exactly, and 448 first so amax = 448
+    bf = torch.from_numpy(vals).to(torch.bfloat16)
+    exact = bf.float().numpy() == vals
+    vals = np.concatenate([[448.0], vals[exact]]).astype(np.float32)
+    D = 128
+    n = (len(vals) + D - 1) // D * D
+    x = np.zeros(n, dtype=np.float32)
+    x[:len(vals)] = vals
+    S = n // D
+    t = torch.from_numpy(x.reshape(1, S, 1, D)).to(torch.bfloat16)
+    plan = run_plan(t, t, t, smooth=False)
+    want = e4m3.encode(x.reshape(S, D))
+    np.testing.assert_array_equal(plan.q8[0, 0, :S].cpu().numpy(), want)
+    np.testing.assert_array_equal(plan.k8[0, 0, :S].cpu().numpy(), want)
+    got_v = plan_head(plan, 0, 0, np.arange(S))["v_codes"][:S]
+    np.testing.assert_array_equal(got_v, want)
+    assert float(plan.q_scale[0, 0, 0]) == 1.0
+
+
+def test_run_twice_is_bitwise_identical():
+    w = workloads.WORKLOADS["mid"]
+    q, k, v = workloads.generate(w)
+    d = dev()
+    import bit_attention_video_smooth_amd as vs
+    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=(16, 3))
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    o1, l1 = [t.clone() for t in plan.run(qd, kd, vd)]
+    p1 = plan.perm.clone()
+    o2, l2 = plan.run(qd, kd, vd)
+    torch.cuda.synchronize(d)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    assert torch.equal(p1, plan.perm)
+
+
+def test_empty_problem_is_a_no_op():
+    import bit_attention_video_smooth_amd as vs
+    d = dev()
+    z = torch.empty(1, 0, 2, 128, dtype=torch.bfloat16, device=d)
+    plan = vs.Plan((1, 0, 2, 128), d)
+    out, lse2 = plan.run(z, z, z)
+    torch.cuda.synchronize(d)
+    assert out.numel() == 0 and lse2.numel() == 0

@@ -26,8 +26,11 @@ Readings where the workload descriptions are loose:
   per head (means ~ N(0, 3^2 I), sigma 0.5, labels uniform at random), and
   K = V W_h + N(0, 1) with W_h orthogonal (QR of a Gaussian matrix).
 
-All draws come from one CPU ``torch.Generator`` seeded per workload, in
-float32, then cast to bf16 (round to nearest even).  Layout [B, S, H, D].
+All draws come from one ``torch.Generator`` seeded per workload, in float32,
+then cast to bf16 (round to nearest even).  Layout [B, S, H, D].  The
+generator lives on the device asked for: the same seed gives the same bytes
+on a given device type (CPU and GPU streams differ), and both the library and
+the oracle always consume one generated copy.
 """
 from dataclasses import dataclass, field
 import math
@@ -83,7 +86,7 @@ def _rope_3d(x, grid, base=10000.0, split=(44, 42, 42)):
     B, S, H, D = x.shape
     assert sum(split) == D
     T, GH, GW = grid
-    s = torch.arange(S, dtype=torch.float64)
+    s = torch.arange(S, dtype=torch.float64, device=x.device)
     pos = [torch.div(s, GH * GW, rounding_mode="floor"),
            torch.remainder(torch.div(s, GW, rounding_mode="floor"), GH),
            torch.remainder(s, GW)]
@@ -91,7 +94,7 @@ def _rope_3d(x, grid, base=10000.0, split=(44, 42, 42)):
     off = 0
     for axis, part in enumerate(split):
         half = part // 2
-        inv = base ** (-torch.arange(half, dtype=torch.float64) * 2.0 / part)
+        inv = base ** (-torch.arange(half, dtype=torch.float64, device=x.device) * 2.0 / part)
         ang = (pos[axis][:, None] * inv[None, :]).to(torch.float32)       # [S, half]
         cos = torch.cos(ang)[None, :, None, :]
         sin = torch.sin(ang)[None, :, None, :]
@@ -108,52 +111,55 @@ def _outliers(v, frac, mult, g):
     n = int(round(frac * S))
     for b in range(B):
         for h in range(H):
-            idx = torch.randperm(S, generator=g)[:n]
+            idx = torch.randperm(S, generator=g, device=v.device)[:n]
             v[b, idx, h, :] *= mult
     return v
 
 
-def generate(w, *, dtype=torch.bfloat16):
-    """Return (q, k, v) CPU tensors [B, S, H, D] of ``dtype`` for workload w
-    (a Workload or its name)."""
+def generate(w, *, dtype=torch.bfloat16, device="cpu"):
+    """Return (q, k, v) tensors [B, S, H, D] of ``dtype`` on ``device`` for
+    workload w (a Workload or its name)."""
     if isinstance(w, str):
         w = WORKLOADS[w]
-    g = torch.Generator().manual_seed(w.seed)
+    device = torch.device(device)
+    g = torch.Generator(device=device).manual_seed(w.seed)
+    rn = lambda *s: torch.randn(*s, generator=g, device=device)  # noqa: E731
+    ru = lambda *s: torch.rand(*s, generator=g, device=device)   # noqa: E731
     B, S, H, D = w.B, w.S, w.H, w.D
     shape = (B, S, H, D)
     e = w.extra
     if w.recipe == "offsets":
-        q = torch.randn(shape, generator=g)
-        k = torch.randn(shape, generator=g)
-        v = torch.randn(shape, generator=g)
+        q = rn(shape)
+        k = rn(shape)
+        v = rn(shape)
         if e["k_off_shared"]:
-            k += e["k_off"] * torch.randn(D, generator=g)
+            k += e["k_off"] * rn(D)
         else:
-            k += e["k_off"] * torch.randn(1, 1, H, D, generator=g)
+            k += e["k_off"] * rn(1, 1, H, D)
         if e["v_off"]:
-            v += e["v_off"] * torch.randn(1, 1, H, D, generator=g)
+            v += e["v_off"] * rn(1, 1, H, D)
         v = _outliers(v, e["out_frac"], e["out_mult"], g)
     elif w.recipe == "rope_drift":
-        q = _rope_3d(_rms_normalize(torch.randn(shape, generator=g)), e["grid"])
-        k = _rope_3d(_rms_normalize(torch.randn(shape, generator=g)), e["grid"])
-        v = torch.randn(shape, generator=g)
-        amp = 0.5 + 1.5 * torch.rand(1, 1, H, D, generator=g)
-        freq = 0.5 + 3.5 * torch.rand(1, 1, H, D, generator=g)
-        phase = 2.0 * math.pi * torch.rand(1, 1, H, D, generator=g)
-        s = (torch.arange(S, dtype=torch.float32) / S).view(1, S, 1, 1)
+        q = _rope_3d(_rms_normalize(rn(shape)), e["grid"])
+        k = _rope_3d(_rms_normalize(rn(shape)), e["grid"])
+        v = rn(shape)
+        amp = 0.5 + 1.5 * ru(1, 1, H, D)
+        freq = 0.5 + 3.5 * ru(1, 1, H, D)
+        phase = 2.0 * math.pi * ru(1, 1, H, D)
+        s = (torch.arange(S, dtype=torch.float32, device=device) / S).view(1, S, 1, 1)
         v += amp * torch.sin(2.0 * math.pi * freq * s + phase)
         v = _outliers(v, e["out_frac"], e["out_mult"], g)
     elif w.recipe == "mixture":
-        q = torch.randn(shape, generator=g)
-        v = torch.empty(shape)
-        k = torch.empty(shape)
+        q = rn(shape)
+        v = torch.empty(shape, device=device)
+        k = torch.empty(shape, device=device)
         for b in range(B):
             for h in range(H):
-                means = e["comp_std"] * torch.randn(e["n_comp"], D, generator=g)
-                lab = torch.randint(0, e["n_comp"], (S,), generator=g)
-                vh = means[lab] + e["noise"] * torch.randn(S, D, generator=g)
-                wq, _ = torch.linalg.qr(torch.randn(D, D, generator=g))
-                kh = vh @ wq + torch.randn(S, D, generator=g)
+                means = e["comp_std"] * rn(e["n_comp"], D)
+                lab = torch.randint(0, e["n_comp"], (S,), generator=g, device=device)
+                vh = means[lab] + e["noise"] * rn(S, D)
+                wq, _ = torch.linalg.qr(rn(D, D).double().cpu())
+                kh = vh @ wq.float().to(device) + rn(S, D)
                 v[b, :, h, :] = vh
                 k[b, :, h, :] = kh
     else:
@@ -163,4 +169,4 @@ def generate(w, *, dtype=torch.bfloat16):
 
 def head_slices(q, k, v, b, h):
     """float32 numpy [S, D] views of one head of bf16 [B, S, H, D] tensors."""
-    return tuple(t[b, :, h, :].float().numpy() for t in (q, k, v))
+    return tuple(t[b, :, h, :].float().cpu().numpy() for t in (q, k, v))
