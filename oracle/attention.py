@@ -48,8 +48,9 @@ Probability casts (``pcast``):
 Precision (``fp32=True``): the pages fix the exponential and K centring at
 FP32 and the operands at E4M3; every quantity that decides a code is formed
 in float32 with one rounding per operation, in the order below, so a kernel
-that computes in FP32 takes the same decisions.  With scores S (the exact dot
-product of the E4M3 codes, rounded to float32):
+that computes in FP32 takes the same decisions.  With scores S (the dot
+product of the E4M3 codes; exactly, rounded to float32, or, with
+``qk_codes``, in the FP8 matrix core's arithmetic, ``matrix_core``):
 
     c_j  = f32(f32(s_Q s_K,j) * c)            c = f32(softmax_scale log2 e)
     s_t  = f32(S_t c_j)                       (only the max uses these)
@@ -75,7 +76,7 @@ the underflow tail) and its two-point extremal row.
 """
 import numpy as np
 
-from . import e4m3
+from . import e4m3, matrix_core
 
 BLOCK = 128
 
@@ -120,7 +121,7 @@ def _f32(x):
 
 def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
                     v_mean=None, vmean_mode="none", q_off=None, pcast="e4m3",
-                    fp32=True, block=BLOCK, return_trace=False):
+                    fp32=True, block=BLOCK, return_trace=False, qk_codes=None):
     """One head, R query rows, the recurrence of the module docstring.
 
     q_hat   [R, D]   query rows (decoded E4M3 codes, or raw values)
@@ -133,6 +134,9 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
     c       score constant softmax_scale * log2 e (float32 when fp32)
     v_mean  [nb, D] (vmean_mode "block") or [D] ("seq") or None ("none")
     q_off   [R] log2 offset added to lse2 (qmu), or None
+    qk_codes (q_codes [R, D], k_codes [>=S, D]) E4M3 bytes: when given, the
+            raw scores are formed in the FP8 matrix core's arithmetic
+            (``matrix_core.mfma_fp8_dot``) instead of exactly
     Returns (O [R, D] float64, lse2 [R] float64) and, with return_trace, a
     dict of per-tile P codes (e4m3/expcast) and row sums for diagnostics.
     """
@@ -154,7 +158,10 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
         n = hi - lo
         kb = k_hat[lo:lo + block]
         vb = v_hat[lo:lo + block]
-        S_raw = rnd(q_hat @ kb[:n].T)                       # [R, n]
+        if qk_codes is not None:
+            S_raw = matrix_core.mfma_fp8_dot_c(qk_codes[0], qk_codes[1][lo:hi])
+        else:
+            S_raw = rnd(q_hat @ kb[:n].T)                   # [R, n]
         cj = rnd(rnd(q_scale * float(k_scale[j])) * c)      # [R]
         s = rnd(S_raw * cj[:, None])
         m_new = np.maximum(m, s.max(axis=1))

@@ -35,12 +35,14 @@ def default_scale(D: int) -> np.float32:
 
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None,
-                            expcast=False, pcast=None, fp32=True):
+                            expcast=False, pcast=None, fp32=True, scores="mfma"):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
     evaluate (default all).  kmeans_kt: (k, iters) or None.  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
+    scores: "mfma" forms QK^T in the FP8 matrix core's arithmetic (the
+    precision in which the kernel decides every P code), "exact" in float64.
     Returns a dict with O, lse2 and every intermediate the GPU path also
     produces.
     """
@@ -93,7 +95,7 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
         e4m3.decode(k_codes), k_scale, e4m3.decode(v_codes), v_scale, S, c,
         v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
-        fp32=fp32)
+        fp32=fp32, qk_codes=(q_codes[rows], k_codes) if scores == "mfma" else None)
     out["O"], out["lse2"] = o, lse2
     return out
 

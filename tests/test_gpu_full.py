@@ -1,0 +1,54 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+bench.py times: inputs generated on the GPU, the whole path run on all heads,
+then sampled heads compared with the oracle (statistics, every code, the
+k-means labels and permutation in full; O and lse2 on evenly spaced rows
+that include the first row, the last row and a row of the ragged last block),
+and properties checked on every head."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import pipeline
+from gpu_util import check_attn, check_intermediates, dev, oracle_head, plan_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(name, expcast=None):
+    import bit_attention_video_smooth_amd as vs
+    w = workloads.WORKLOADS[name]
+    d = dev()
+    print(f"[full] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={expcast}", flush=True)
+    q, k, v = workloads.generate(w, device=d)
+    ec = w.expcast if expcast is None else expcast
+    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=w.kmeans, expcast=ec)
+    plan.run(q, k, v)
+    torch.cuda.synchronize(d)
+    # properties on every head
+    assert torch.isfinite(plan.out).all() and torch.isfinite(plan.lse2).all()
+    if plan.perm is not None:
+        srt = torch.sort(plan.perm, dim=-1).values
+        assert torch.equal(srt, torch.arange(w.S, device=d, dtype=srt.dtype).expand_as(srt))
+        lab_sorted = torch.gather(plan.labels, -1, plan.perm.long())
+        assert bool((lab_sorted[..., 1:] >= lab_sorted[..., :-1]).all())
+    return w, q, k, v, plan, ec
+
+
+@pytest.mark.parametrize("name,expcast,heads,nrows", [
+    ("mid", None, (0, 7), 64),
+    ("live", None, (0, 27, 55), 32),
+    ("grouped", None, (0, 39), 32),
+    ("long", True, (0, 55), 24),
+    ("long", False, (31,), 24),
+])
+def test_full_size(name, expcast, heads, nrows):
+    w, q, k, v, plan, ec = _run(name, expcast)
+    rows = pipeline.sample_rows(w.S, nrows)
+    for h in heads:
+        print(f"[full] {name} head {h}: oracle", flush=True)
+        ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=w.kmeans, expcast=ec)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, w.S, label=f"{name} h{h}")
+        np.testing.assert_allclose(got["q_mu"][rows], ref["q_off"], rtol=1e-5, atol=1e-5)
+        check_attn(got["O"], got["lse2"], ref, label=f"{name} ec={ec} h{h}")
