@@ -8,23 +8,29 @@
 // sum.  Output O and log2-LSE as in FastVideo PR #2048 ("Test Results").
 //
 // gfx950 mapping
-//   grid (ceil(S/128), H, B); 256 threads = 4 waves; one workgroup owns 128
-//   queries (one Q quantization block, so s_Q is uniform), each wave 32.
-//   Per 128-key tile j:
+//   1-D grid over (batch, head, 128-query block), ordered so that each XCD
+//   (workgroup id mod 8) walks a contiguous range of heads: the K/V of a head
+//   then streams through one XCD's L2 for all its query blocks.
+//   256 threads = 4 waves; a workgroup owns 128 queries (one Q quantization
+//   block, so s_Q is uniform), each wave 32.  Per 128-key tile j:
 //     S^T = K_j Q^T on v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64 channels
-//       from LDS, B = the wave's 32 queries held in registers), 4 key
-//       sub-tiles x D/64 k-steps.  In the accumulator a lane holds one query
-//       (lane % 32) and 16 keys per sub-tile, so the row max / row sum need
-//       one exchange with the other half-wave only.
+//       from LDS, B = the wave's 32 queries, held in registers for the whole
+//       loop).  A lane owns one query (lane % 32) and 16 keys per 32-key
+//       sub-tile, so the tile max / row sum need one cross-half exchange.
 //     P is formed in registers and packed to E4M3 straight into the B operand
-//       of the PV product: the accumulator layout of two key sub-tiles is
-//       exactly the 64-token k-step the PV MFMA consumes, given that V is
-//       stored with the matching token order (vs_quantize_residual).
-//     O^T += V_j^T P^T on the same MFMA (A = 32 channels x 64 tokens, LDS).
-//   K and V tiles (16 KB each at D = 128) are double-buffered in LDS through
-//   registers; 16-byte chunks are XOR-swizzled by row so the 128-bit operand
-//   reads of 8 consecutive rows hit distinct banks.  The block means of V for
-//   the tile ride along in LDS.
+//       of PV: the accumulator layout of two key sub-tiles is exactly one
+//       64-token k-step of the PV MFMA, given that V is stored in the matching
+//       token order (vs_quantize_residual).
+//     O^T: tmp = V_j^T P^T on the same MFMA (A = 32 channels x 64 tokens),
+//       acc = alpha acc + s_V,j/256 tmp (alpha applied only when some row's max
+//       moved), and the rank-one restore acc += mu_j (x) l_j as
+//       v_mfma_f32_32x32x1_2b_f32 outer products (one per pair of channel
+//       tiles) instead of D FMAs per lane.
+//   K and V tiles (16 KB each at D = 128) are double-buffered in LDS and
+//   filled with global_load_lds_dwordx4 (no staging registers): each lane's
+//   16-byte source is chosen so the LDS image is the XOR-swizzled tile, and
+//   the 128-bit operand reads of 8 consecutive rows hit distinct banks.  The
+//   last (possibly ragged) tile is peeled so the main loop carries no mask.
 #include <float.h>
 
 #include "common.h"
@@ -32,13 +38,9 @@
 namespace vs {
 namespace {
 
-constexpr float kExpcastK0 = 119.66015f;   // 120 - 4 (log2(1.5) - 1/2)
+typedef float v32f __attribute__((ext_vector_type(32)));
 
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (row & 7) : ((row >> 1) & 3);
-}
-__device__ __forceinline__ int v_swz(int row) { return row & 7; }
+constexpr float kExpcastK0 = 119.66015f;   // 120 - 4 (log2(1.5) - 1/2)
 
 __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   v8i r;
@@ -51,23 +53,61 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// 16-byte asynchronous global -> LDS copy; lane i of the wave writes
+// dst + 16 i (dst is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// Source chunk (lane-dependent part of a tile DMA) such that LDS chunk
+// position `lane` of a row holds logical chunk position ^ swizzle(row):
+// rows of 8 chunks swizzle with row & 7, rows of 4 with (row >> 1) & 3.  The
+// row index inside one 64-chunk DMA block only affects the uniform part.
+template <int ROWCHUNKS>
+__device__ __forceinline__ int dma_src_chunk(int lane) {
+  if (ROWCHUNKS == 8) return (lane & ~7) | ((lane & 7) ^ ((lane >> 3) & 7));
+  return (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
+}
+
+template <int ROWCHUNKS>
+__device__ __forceinline__ int row_swz(int row) {
+  return ROWCHUNKS == 8 ? (row & 7) : ((row >> 1) & 3);
+}
+
 template <int D, bool EXPCAST, int VMEAN>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, const float* __restrict__ q_mu, int S, int H,
-    int nb, float c_log2, float* __restrict__ out, float* __restrict__ lse2) {
+    int nb, int total, float c_log2, float* __restrict__ out, float* __restrict__ lse2) {
   constexpr int KD = D / 64;                 // k-steps of the QK product
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
   constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
-  constexpr int CPT = TB / 16 / 256;         // 16-byte chunks per thread per tile
-  constexpr int KCH = D / 16;                // 16-byte chunks per K row
-  __shared__ __attribute__((aligned(16))) uint8_t sk[2][TB];
-  __shared__ __attribute__((aligned(16))) uint8_t sv[2][TB];
+  constexpr int KRC = D / 16;                // 16-byte chunks per K row
+  constexpr int NDMA = TB / 16 / 64 / 4;     // DMA instructions per wave, tile and tensor
+  __shared__ __attribute__((aligned(1024))) uint8_t sk[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv[2][TB];
   __shared__ __attribute__((aligned(16))) float smu[2][D];
 
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // ---- workgroup -> (b, h, query block), XCD-contiguous ----
+  int qb, h, b;
+  {
+    const int L = blockIdx.x;
+    const int xcd = L & 7, idx = L >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int logical = xcd < rem ? xcd * (per + 1) + idx
+                                  : rem * (per + 1) + (xcd - rem) * per + idx;
+    qb = logical % nb;
+    const int bh_l = logical / nb;
+    h = bh_l % H;
+    b = bh_l / H;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t bh = static_cast<size_t>(b) * H + h;
@@ -79,45 +119,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   {
     const uint8_t* qp = q8 + (bh * S_pad + qrow) * D + 32 * hh;
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) {
-      const uint4 a = *reinterpret_cast<const uint4*>(qp + 64 * kd);
-      const uint4 c = *reinterpret_cast<const uint4*>(qp + 64 * kd + 16);
-      qa[kd] = make_v8i(a, c);
-    }
+    for (int kd = 0; kd < KD; ++kd)
+      qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qp + 64 * kd),
+                        *reinterpret_cast<const uint4*>(qp + 64 * kd + 16));
   }
   const float sq = q_scale[bh * nb + qb];
 
   const uint8_t* kbase = k8 + bh * S_pad * D;
-  const uint8_t* vbase = v8 + bh * nb * static_cast<size_t>(D) * kBlock;
+  const uint8_t* vbase = v8 + bh * nb * static_cast<size_t>(TB);
   const float* mubase = (VMEAN == VS_VMEAN_BLOCK) ? v_mean + bh * nb * D : nullptr;
+  const float* ksc = k_scale + bh * nb;
+  const float* vsc = v_scale + bh * nb;
 
-  uint4 kst[CPT], vst[CPT];
-  float must = 0.0f;
-  auto load_tile = [&](int j) {
-    const uint4* kg = reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(j) * TB);
-    const uint4* vg = reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(j) * TB);
+  // per-lane DMA source offsets (bytes inside a tile) and operand read bases
+  const int k_src = dma_src_chunk<KRC>(lane) * 16;
+  const int v_src = dma_src_chunk<8>(lane) * 16;
+  int k_rd[KD][2], v_rd[2][2];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      kst[i] = kg[tid + 256 * i];
-      vst[i] = vg[tid + 256 * i];
-    }
-    if (VMEAN == VS_VMEAN_BLOCK && tid < D) must = mubase[static_cast<size_t>(j) * D + tid];
-  };
-  auto store_tile = [&](int buf) {
+  for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int g = tid + 256 * i;
-      const int kr = g / KCH, kc = g % KCH;
-      *reinterpret_cast<uint4*>(&sk[buf][kr * D + ((kc ^ k_swz<D>(kr)) << 4)]) = kst[i];
-      const int vr = g >> 3, vc = g & 7;
-      *reinterpret_cast<uint4*>(&sv[buf][vr * kBlock + ((vc ^ v_swz(vr)) << 4)]) = vst[i];
-    }
-    if (VMEAN == VS_VMEAN_BLOCK && tid < D) smu[buf][tid] = must;
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+    for (int e = 0; e < 2; ++e)
+      k_rd[kd][e] = l32 * D + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      v_rd[kk][e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
 
   float m = -INFINITY, l = 0.0f;
   v16f acc[DT];
@@ -126,28 +153,45 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
+#define VS_ISSUE_TILE(J, BUF)                                                          \
+  do {                                                                                 \
+    const uint8_t* kg_ = kbase + static_cast<size_t>(J) * TB;                          \
+    const uint8_t* vg_ = vbase + static_cast<size_t>(J) * TB;                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < NDMA; ++i_) {                              \
+      const int base_ = (wave * NDMA + i_) * 1024;                                     \
+      dma16(kg_ + base_ + k_src, &sk[(BUF)][base_]);                                   \
+      dma16(vg_ + base_ + v_src, &sv[(BUF)][base_]);                                   \
+    }                                                                                  \
+    if (VMEAN == VS_VMEAN_BLOCK && wave == 0 && lane < D / 4)                          \
+      dma16(mubase + static_cast<size_t>(J) * D + 4 * lane, &smu[(BUF)][0]);           \
+  } while (0)
+
+  VS_ISSUE_TILE(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   for (int j = 0; j < nb; ++j) {
     const int buf = j & 1;
-    if (j + 1 < nb) load_tile(j + 1);
+    const bool last = j == nb - 1;
+    if (!last) VS_ISSUE_TILE(j + 1, buf ^ 1);
+    const uint8_t* skb = sk[buf];
+    const uint8_t* svb = sv[buf];
 
     // ---- S^T = K_j Q^T : 4 sub-tiles of 32 keys ----
     v16f s[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const uint8_t* kr = skb + t * 32 * D;
+      s[t] = mfma_fp8(make_v8i(lds_read16(kr + k_rd[0][0]), lds_read16(kr + k_rd[0][1])), qa[0],
+                      v16f{});
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-      const int kr = 32 * t + l32;
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) {
-        const int c0 = 4 * kd + 2 * hh;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(&sk[buf][kr * D + ((c0 ^ k_swz<D>(kr)) << 4)]);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(&sk[buf][kr * D + (((c0 + 1) ^ k_swz<D>(kr)) << 4)]);
-        s[t] = mfma_fp8(make_v8i(a0, a1), qa[kd], s[t]);
-      }
+      for (int kd = 1; kd < KD; ++kd)
+        s[t] = mfma_fp8(make_v8i(lds_read16(kr + k_rd[kd][0]), lds_read16(kr + k_rd[kd][1])),
+                        qa[kd], s[t]);
     }
-    // keys past S (last tile only): -inf, so they drop out of the max and
-    // give p = 0 / code 0
-    if (j == nb - 1 && (S & (kBlock - 1))) {
+    // keys past S (ragged last tile only): -inf drops them from the max and
+    // gives p = 0 / code 0
+    if (last && (S & (kBlock - 1))) {
       const int valid = S - j * kBlock;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -163,7 +207,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float cj = (sq * k_scale[bh * nb + j]) * c_log2;
+    const float cj = (sq * ksc[j]) * c_log2;
     const float m_new = __builtin_fmaxf(m, mx * cj);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
 
@@ -212,36 +256,50 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     ell *= (1.0f / 256.0f);
     l = alpha * l + ell;
 
-    // ---- O^T = alpha O^T + s_V (V^T P^T) + ell mu_j ----
-    const float svj = v_scale[bh * nb + j] * (1.0f / 256.0f);
+    // ---- O^T = alpha O^T + s_V/256 (V^T P^T) + mu (x) l ----
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    }
+    const float svj = vsc[j] * (1.0f / 256.0f);
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      v16f tmp;
+      const uint8_t* vr = svb + t * 32 * kBlock;
+      v16f tmp = mfma_fp8(make_v8i(lds_read16(vr + v_rd[0][0]), lds_read16(vr + v_rd[0][1])), pb[0],
+                          v16f{});
+      tmp = mfma_fp8(make_v8i(lds_read16(vr + v_rd[1][0]), lds_read16(vr + v_rd[1][1])), pb[1], tmp);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmp[r] = 0.0f;
-      const int vr = 32 * t + l32;
+      for (int r = 0; r < 16; ++r) acc[t][r] = __builtin_fmaf(tmp[r], svj, acc[t][r]);
+    }
+    if (VMEAN == VS_VMEAN_BLOCK) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int c0 = 4 * kk + 2 * hh;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(&sv[buf][vr * kBlock + ((c0 ^ v_swz(vr)) << 4)]);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(&sv[buf][vr * kBlock + (((c0 + 1) ^ v_swz(vr)) << 4)]);
-        tmp = mfma_fp8(make_v8i(a0, a1), pb[kk], tmp);
-      }
+      for (int pr = 0; pr < DT / 2; ++pr) {
+        // lanes 0-31 carry mu of channel tile 2pr, lanes 32-63 of tile 2pr+1
+        const float mu = smu[buf][64 * pr + lane];
+        v32f c2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float o = __builtin_fmaf(tmp[r], svj, acc[t][r] * alpha);
-        if (VMEAN == VS_VMEAN_BLOCK)
-          o = __builtin_fmaf(ell, smu[buf][32 * t + 8 * (r >> 2) + 4 * hh + (r & 3)], o);
-        acc[t][r] = o;
+        for (int r = 0; r < 16; ++r) {
+          c2[r] = acc[2 * pr][r];
+          c2[16 + r] = acc[2 * pr + 1][r];
+        }
+        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[2 * pr][r] = c2[r];
+          acc[2 * pr + 1][r] = c2[16 + r];
+        }
       }
     }
     m = m_new;
 
-    if (j + 1 < nb) {
-      store_tile(buf ^ 1);
+    if (!last) {
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
+#undef VS_ISSUE_TILE
 
   // ---- epilogue: O = acc / l (+ sequence mean), lse2 = m + log2 l + q_mu ----
   if (qrow < S) {
@@ -269,19 +327,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 }
 
 template <int D, bool EXPCAST>
-void launch_vm(int vmean_mode, dim3 grid, hipStream_t st, const uint8_t* q8, const float* qs,
+void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
                const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
                const float* vm, const float* qmu, int S, int H, int nb, float c, float* out,
                float* lse2) {
+  const dim3 grid(total), block(256);
   if (vmean_mode == VS_VMEAN_BLOCK)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK>), grid, dim3(256), 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, c, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK>), grid, block, 0, st, q8, qs, k8,
+                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
   else if (vmean_mode == VS_VMEAN_SEQ)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ>), grid, dim3(256), 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, c, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ>), grid, block, 0, st, q8, qs, k8,
+                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE>), grid, dim3(256), 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, c, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE>), grid, block, 0, st, q8, qs, k8,
+                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
 }
 
 }  // namespace
@@ -306,19 +365,20 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   const void* ptrs[] = {q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, out, lse2};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
-  if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
-
   const int nb = n_blocks(S);
+  const long long total = static_cast<long long>(B) * H * nb;
+  if (total > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
+
   const float c = softmax_scale * 1.44269504088896341f;
-  const dim3 grid(nb, H, B);
   hipStream_t st = as_stream(stream);
   const bool ec = (flags & VS_EXPCAST) != 0;
+  const int tot = static_cast<int>(total);
   if (D == 128) {
-    if (ec) launch_vm<128, true>(vmean_mode, grid, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
-    else launch_vm<128, false>(vmean_mode, grid, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
   } else {
-    if (ec) launch_vm<64, true>(vmean_mode, grid, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
-    else launch_vm<64, false>(vmean_mode, grid, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
   }
   return launch_status();
 }
