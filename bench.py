@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--expcast", type=int, default=None, help="override the workload's ExpCast flag")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a known-size "
+                         "kernel that scales FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -83,6 +86,12 @@ def main():
     q, k, v = workloads.generate(w, device=dev)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast)
     torch.cuda.synchronize(dev)
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     for _ in range(args.warmup):
         plan.run(q, k, v)

@@ -21,16 +21,20 @@
 //       of PV: the accumulator layout of two key sub-tiles is exactly one
 //       64-token k-step of the PV MFMA, given that V is stored in the matching
 //       token order (vs_quantize_residual).
-//     O^T: tmp = V_j^T P^T on the same MFMA (A = 32 channels x 64 tokens),
-//       acc = alpha acc + s_V,j/256 tmp (alpha applied only when some row's max
-//       moved), and the rank-one restore acc += mu_j (x) l_j as
+//     O^T: acc = alpha acc (only when some row's max moved), then
+//       acc += 2^e_j 2^-8 V_j^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (A =
+//       32 channels x 64 tokens): the power-of-two V block scale and P's 2^8
+//       are E8M0 operand scales, so the product accumulates straight into acc;
+//       then the rank-one restore acc += mu_j (x) l_j as
 //       v_mfma_f32_32x32x1_2b_f32 outer products (one per pair of channel
 //       tiles) instead of D FMAs per lane.
 //   K and V tiles (16 KB each at D = 128) are double-buffered in LDS and
 //   filled with global_load_lds_dwordx4 (no staging registers): each lane's
 //   16-byte source is chosen so the LDS image is the XOR-swizzled tile, and
-//   the 128-bit operand reads of 8 consecutive rows hit distinct banks.  The
-//   last (possibly ragged) tile is peeled so the main loop carries no mask.
+//   the 128-bit operand reads of 16 consecutive rows hit distinct banks
+//   (gfx950's LDS serves a 128-bit read over 64 banks: rows of 128 B need the
+//   chunk index XORed with (row >> 1) & 7).  The ragged last tile's mask sits
+//   behind a uniform branch.
 #include <float.h>
 
 #include "common.h"
@@ -53,6 +57,12 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Same product with E8M0 operand scales (byte b means 2^(b - 127)).
+__device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, const v16f& c,
+                                                int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -64,19 +74,25 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
                                    (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-// Source chunk (lane-dependent part of a tile DMA) such that LDS chunk
-// position `lane` of a row holds logical chunk position ^ swizzle(row):
-// rows of 8 chunks swizzle with row & 7, rows of 4 with (row >> 1) & 3.  The
-// row index inside one 64-chunk DMA block only affects the uniform part.
-template <int ROWCHUNKS>
-__device__ __forceinline__ int dma_src_chunk(int lane) {
-  if (ROWCHUNKS == 8) return (lane & ~7) | ((lane & 7) ^ ((lane >> 3) & 7));
-  return (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
-}
-
+// XOR swizzle of a row's 16-byte chunk index: rows of 8 chunks (128 B) use
+// (row >> 1) & 7, rows of 4 chunks (64 B) use (row >> 1) & 3.
 template <int ROWCHUNKS>
 __device__ __forceinline__ int row_swz(int row) {
-  return ROWCHUNKS == 8 ? (row & 7) : ((row >> 1) & 3);
+  return ROWCHUNKS == 8 ? ((row >> 1) & 7) : ((row >> 1) & 3);
+}
+
+// Source chunk, inside one 64-chunk (1 KB) DMA block `blk` of a tile, for the
+// LDS chunk position `lane`: that position holds logical chunk
+// (position ^ swizzle(row)) of its row.  Only the parity of the block index
+// matters for 8-chunk rows (8 rows per block); none for 4-chunk rows.
+template <int ROWCHUNKS>
+__device__ __forceinline__ int dma_src_chunk(int lane, int blk) {
+  if (ROWCHUNKS == 8) {
+    const int row = 8 * blk + (lane >> 3);
+    return (lane & ~7) | ((lane & 7) ^ row_swz<8>(row));
+  }
+  const int row = 16 * blk + (lane >> 2);
+  return (lane & ~3) | ((lane & 3) ^ row_swz<4>(row));
 }
 
 template <int D, bool EXPCAST, int VMEAN>
@@ -108,7 +124,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     h = bh_l % H;
     b = bh_l / H;
   }
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t S_pad = static_cast<size_t>(nb) * kBlock;
@@ -131,9 +148,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const float* ksc = k_scale + bh * nb;
   const float* vsc = v_scale + bh * nb;
 
-  // per-lane DMA source offsets (bytes inside a tile) and operand read bases
-  const int k_src = dma_src_chunk<KRC>(lane) * 16;
-  const int v_src = dma_src_chunk<8>(lane) * 16;
+  // per-lane DMA source offsets (bytes inside a 1 KB block; even and odd
+  // blocks) and operand read bases
+  const int k_src[2] = {dma_src_chunk<KRC>(lane, 0) * 16, dma_src_chunk<KRC>(lane, 1) * 16};
+  const int v_src[2] = {dma_src_chunk<8>(lane, 0) * 16, dma_src_chunk<8>(lane, 1) * 16};
   int k_rd[KD][2], v_rd[2][2];
 #pragma unroll
   for (int kd = 0; kd < KD; ++kd)
@@ -159,8 +177,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint8_t* vg_ = vbase + static_cast<size_t>(J) * TB;                          \
     _Pragma("unroll") for (int i_ = 0; i_ < NDMA; ++i_) {                              \
       const int base_ = (wave * NDMA + i_) * 1024;                                     \
-      dma16(kg_ + base_ + k_src, &sk[(BUF)][base_]);                                   \
-      dma16(vg_ + base_ + v_src, &sv[(BUF)][base_]);                                   \
+      dma16(kg_ + base_ + k_src[i_ & 1], &sk[(BUF)][base_]);                           \
+      dma16(vg_ + base_ + v_src[i_ & 1], &sv[(BUF)][base_]);                           \
     }                                                                                  \
     if (VMEAN == VS_VMEAN_BLOCK && wave == 0 && lane < D / 4)                          \
       dma16(mubase + static_cast<size_t>(J) * D + 4 * lane, &smu[(BUF)][0]);           \
@@ -256,22 +274,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     ell *= (1.0f / 256.0f);
     l = alpha * l + ell;
 
-    // ---- O^T = alpha O^T + s_V/256 (V^T P^T) + mu (x) l ----
+    // ---- O^T = alpha O^T + 2^e_j 2^-8 (V^T P^T) + mu (x) l ----
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
     }
-    const float svj = vsc[j] * (1.0f / 256.0f);
+    // E8M0 byte of the V block scale 2^e_j (a normal float: its exponent
+    // field), and 2^-8 for P's prescale
+    const int sv_e8 = (__float_as_int(vsc[j]) >> 23) & 0xFF;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const uint8_t* vr = svb + t * 32 * kBlock;
-      v16f tmp = mfma_fp8(make_v8i(lds_read16(vr + v_rd[0][0]), lds_read16(vr + v_rd[0][1])), pb[0],
-                          v16f{});
-      tmp = mfma_fp8(make_v8i(lds_read16(vr + v_rd[1][0]), lds_read16(vr + v_rd[1][1])), pb[1], tmp);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] = __builtin_fmaf(tmp[r], svj, acc[t][r]);
+      acc[t] = mfma_fp8_scaled(make_v8i(lds_read16(vr + v_rd[0][0]), lds_read16(vr + v_rd[0][1])),
+                               pb[0], acc[t], sv_e8, 127 - 8);
+      acc[t] = mfma_fp8_scaled(make_v8i(lds_read16(vr + v_rd[1][0]), lds_read16(vr + v_rd[1][1])),
+                               pb[1], acc[t], sv_e8, 127 - 8);
     }
     if (VMEAN == VS_VMEAN_BLOCK) {
 #pragma unroll

@@ -6,6 +6,10 @@
 // residual is quantized.  The block's scale is set by its largest entry
 // (VC-Attention abstract): scale = amax / 448, codes = E4M3(x * (448/amax)).
 //
+// The V residual's scale is the power of two 2^e, e the smallest integer with
+// amax <= 448 * 2^e (e >= -126): an E8M0 block scale that the FP8 matrix core
+// applies itself during PV.
+//
 // One workgroup per (block, head, batch).  The block (128 tokens x D) is read
 // once from HBM into registers (64 values per thread at D = 128), reduced to
 // its amax, encoded with the hardware E4M3 conversion (round to nearest even
@@ -139,7 +143,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
 }
 
-// Residual V: codes transposed per block, [D][128] in the MFMA token order.
+// Smallest e >= -126 with amax <= 448 * 2^e (0 when amax == 0).
+__device__ __forceinline__ int pow2_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = ilogbf(amax) - 8;
+  while (amax > ldexpf(448.0f, e)) ++e;
+  while (e > -126 && amax <= ldexpf(448.0f, e - 1)) --e;
+  return e < -126 ? -126 : e;
+}
+
+// Residual V: codes transposed per block, [D][128] in the MFMA token order,
+// power-of-two scale.
 template <int D>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
@@ -167,9 +181,9 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
     }
   }
   const float amax = block_amax(a, red4);
-  float scale, inv;
-  scale_of(amax, scale, inv);
-  if (threadIdx.x == 0) scale_out[bh * nb + j] = scale;
+  const int e = pow2_exponent(amax);
+  const float inv = ldexpf(1.0f, -e);
+  if (threadIdx.x == 0) scale_out[bh * nb + j] = ldexpf(1.0f, e);
 
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {

@@ -114,13 +114,17 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
  *                   t(p) = 64*(p/64) + 32*((p%32)/16) + 8*((p%16)/4)
  *                          + 4*((p%64)/32) + p%4
  *                 (the order the attention kernel's FP8 MFMA consumes).
- *   q_scale, k_scale, v_scale  out f32 [B,H,nb]: dequantization scales.
+ *   q_scale, k_scale, v_scale  out f32 [B,H,nb]: dequantization scales
+ *                 (v_scale is a power of two, see below).
  *   q_mu          out f32 [B,H,S]: c * (q . k_mean) with c = softmax_scale *
  *                 log2(e), from the bf16 q; required iff k_mean != NULL.
  * Per block: x = float32 input (minus the mean, one float32 subtraction),
  * amax = max |x| over the valid tokens and D channels, scale = amax / 448,
  * code = E4M3(x * (448 / amax)) round-to-nearest-even, saturating at 448
  * (448 / amax clamped to FLT_MAX); amax == 0 gives scale 1 and codes 0.
+ * The V residual uses the power-of-two scale 2^e, e the smallest integer
+ * >= -126 with amax <= 448 * 2^e, codes = E4M3(x * 2^-e): an E8M0 block scale
+ * that the FP8 matrix core applies exactly during PV.
  */
 int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, int kv_layout, int B, int S, int H,

@@ -6,8 +6,8 @@ Test infrastructure (see ``oracle/__init__``).
    K and V permuted together (``kmeans``);
 2. exact statistics: mu_K over the sequence, mu_V per 128-token block (or
    over the sequence) (``smoothing``);
-3. per-block E4M3 quantization of Q, of K - mu_K and of the V residual, and
-   qmu = c q.mu_K from the bf16 q (``smoothing``);
+3. per-block E4M3 quantization of Q, of K - mu_K and of the V residual
+   (power-of-two scale), and qmu = c q.mu_K from the bf16 q (``smoothing``);
 4. the tiled recurrence with the rank-one mean restore and the chosen P cast
    (``attention``).
 
@@ -85,7 +85,7 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
 
     q_codes, q_scale = smoothing.quantize_blocks(q)
     k_codes, k_scale = smoothing.quantize_blocks(kc)
-    v_codes, v_scale = smoothing.quantize_blocks(vr)
+    v_codes, v_scale = smoothing.quantize_blocks(vr, pow2=True)
     out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
                k_scale=k_scale, v_codes=v_codes, v_scale=v_scale, q_off=q_off)
 

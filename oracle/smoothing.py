@@ -20,10 +20,16 @@ Sources
   "centralize V, restore its sequence mean after attention".
 * Block quantization scale: one scale per block set by the block's largest
   entry (VC-Attention abstract: "a block's quantization scale is set by its
-  largest entries").  Reading: scale = amax / 448 over the block's valid
-  tokens and all channels, in FP32; codes = E4M3(x * (448 / amax)) in FP32.
-  A block with amax == 0 uses scale 1 (all codes 0).  448 / amax is clamped
-  to the largest finite float32 so a denormal amax cannot make it infinite.
+  largest entries").  Reading for Q and K: scale = amax / 448 over the
+  block's valid tokens and all channels, in FP32; codes = E4M3(x * (448 /
+  amax)) in FP32.  A block with amax == 0 uses scale 1 (all codes 0).
+  448 / amax is clamped to the largest finite float32 so a denormal amax
+  cannot make it infinite.  Reading for the V residual: the scale is the
+  power of two 2^e with e the smallest integer such that amax <= 448 * 2^e
+  (e >= -126; e = 0 when amax == 0), codes = E4M3(x * 2^-e).  A power-of-two
+  block scale (the E8M0 block scale of MX formats) is applied by the FP8
+  matrix core itself during PV, exactly; it leaves every value's relative
+  precision unchanged and only lets the block maximum land in (224, 448].
 
 Pinned by tests/test_oracle_quant.py (amax element -> +-448, reconstruction
 error within half an E4M3 step, padding, exact centring, mean error of the
@@ -87,11 +93,25 @@ def residual_blocks(v, block_means, block: int = BLOCK) -> np.ndarray:
     return (np.asarray(v, dtype=np.float32) - block_means[idx]).astype(np.float32)
 
 
-def quantize_blocks(x, block: int = BLOCK):
+def pow2_exponent(amax) -> int:
+    """Smallest integer e >= -126 with amax <= 448 * 2^e (0 for amax == 0)."""
+    a = float(amax)
+    if a == 0.0:
+        return 0
+    e = int(np.floor(np.log2(a))) - 8
+    while a > 448.0 * 2.0 ** e:
+        e += 1
+    while e > -126 and a <= 448.0 * 2.0 ** (e - 1):
+        e -= 1
+    return max(e, -126)
+
+
+def quantize_blocks(x, block: int = BLOCK, pow2: bool = False):
     """Per-block E4M3 quantization of a float32 [S, D] array.
 
     Returns (codes uint8 [nb*block, D], scale float32 [nb]).  Rows past S are
     padding and get code 0.  Dequantized value = decode(code) * scale.
+    pow2: power-of-two scale (the V residual reading above).
     """
     x = np.asarray(x, dtype=np.float32)
     S, D = x.shape
@@ -101,6 +121,11 @@ def quantize_blocks(x, block: int = BLOCK):
     for j in range(nb):
         xb = x[j * block:min(S, (j + 1) * block)]
         amax = np.float32(np.max(np.abs(xb)))
+        if pow2:
+            e = pow2_exponent(amax)
+            scale[j] = np.float32(2.0 ** e)
+            codes[j * block:j * block + xb.shape[0]] = e4m3.encode(xb.astype(np.float64) * 2.0 ** -e)
+            continue
         if amax > 0:
             s = np.float32(amax / np.float32(448.0))
             inv = np.float32(np.float32(448.0) / amax)

@@ -115,3 +115,23 @@ def test_q_log2_offset_is_the_row_shift_of_centring():
     z = float(c) * (q.astype(np.float64) @ k.T.astype(np.float64))
     zc = float(c) * (q.astype(np.float64) @ (k.astype(np.float64) - mu.astype(np.float64)).T)
     np.testing.assert_allclose(z - zc, np.repeat(off[:, None], 50, axis=1), rtol=0, atol=1e-12)
+
+
+def test_pow2_scale_is_the_smallest_fitting_power_of_two():
+    rng = np.random.default_rng(6)
+    for amax in [1e-30, 0.3, 1.0, 447.0, 448.0, 448.5, 896.0, 897.0, 3e5]:
+        e = smoothing.pow2_exponent(np.float32(amax))
+        assert amax <= 448 * 2.0 ** e and (e == -126 or amax > 448 * 2.0 ** (e - 1))
+    assert smoothing.pow2_exponent(0.0) == 0
+    x = (rng.standard_normal((300, 32)) * rng.uniform(0.01, 50, (300, 1))).astype(np.float32)
+    codes, scale = smoothing.quantize_blocks(x, pow2=True)
+    for j in range(3):
+        xb = x[j * 128:min(300, (j + 1) * 128)]
+        e = np.log2(float(scale[j]))
+        assert e == np.round(e)                                    # a power of two
+        m = np.abs(e4m3.decode(codes[j * 128:j * 128 + len(xb)])).max()
+        assert 224 < m <= 448                                      # the max lands in (224, 448]
+        rec = e4m3.decode(codes[j * 128:j * 128 + len(xb)]) * float(scale[j])
+        y = np.abs(xb.astype(np.float64)) / float(scale[j])
+        assert np.all(np.abs(rec - xb) <= e4m3.ulp_half(y) * float(scale[j]) * 1.0000001)
+    assert np.all(codes[300:] == 0)
