@@ -20,7 +20,10 @@
 //     P is formed in registers and packed to E4M3 straight into the B operand
 //       of PV: the accumulator layout of two key sub-tiles is exactly one
 //       64-token k-step of the PV MFMA, given that V is stored in the matching
-//       token order (vs_quantize_residual).
+//       token order (vs_quantize_residual).  The tile row sum l_j of those
+//       E4M3 probabilities is one more product on the matrix core (the P
+//       codes against an all-ones A operand), which replaces 64 adds, the
+//       ExpCast decode and the cross-half exchange per lane.
 //     O^T: acc = alpha acc (only when some row's max moved), then
 //       acc += 2^e_j 2^-8 V_j^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (A =
 //       32 channels x 64 tokens): the power-of-two V block scale and P's 2^8
@@ -67,13 +70,6 @@ __device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// 16-byte asynchronous global -> LDS copy; lane i of the wave writes
-// dst + 16 i (dst is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-
 // XOR swizzle of a row's 16-byte chunk index: rows of 8 chunks (128 B) use
 // (row >> 1) & 7, rows of 4 chunks (64 B) use (row >> 1) & 3.
 template <int ROWCHUNKS>
@@ -95,6 +91,258 @@ __device__ __forceinline__ int dma_src_chunk(int lane, int blk) {
   return (lane & ~3) | ((lane & 3) ^ row_swz<4>(row));
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, gfx9 data format).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16-byte asynchronous buffer -> LDS copy: lane i reads base + soff + voff
+// and writes dst + 16 i (dst and soff wave-uniform).
+__device__ __forceinline__ void dma16(rsrc_t rs, int voff, int soff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
+
+// Uniform values and per-lane constants of one workgroup.
+template <int D>
+struct Ctx {
+  rsrc_t krs, vrs, murs;                 // this head's K codes, V codes, V block means
+  const float* ksc;                      // K block scales of this head
+  const float* vsc;                      // V block scales of this head
+  float sq, c_log2;
+  int nb, S, wave, hh, lane;
+  int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
+  int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
+  v8i qa[D / 64];                        // this lane's query, B operand of QK
+  v8i ones;                              // E4M3 ones, A operand of the row sums
+};
+
+// Recurrence state of one wave: raw scores of the tile to be processed
+// next, their maximum, the running max / sum and O^T.
+template <int D>
+struct State {
+  v16f s[4];
+  v16f acc[D / 32];
+  float mx, m, l;
+};
+
+template <int D>
+__device__ __forceinline__ void issue_k(const Ctx<D>& c, int j, uint8_t* dst) {
+  constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int base = (c.wave * NDMA + i) * 1024;
+    dma16(c.krs, c.k_src[i & 1], j * TB + base, dst + base);
+  }
+}
+
+template <int D, int VMEAN>
+__device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, float* mu_dst) {
+  constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int base = (c.wave * NDMA + i) * 1024;
+    dma16(c.vrs, c.v_src[i & 1], j * TB + base, dst + base);
+  }
+  if (VMEAN == VS_VMEAN_BLOCK && c.wave == 0 && c.lane < D / 4)
+    dma16(c.murs, 16 * c.lane, j * D * 4, mu_dst);
+}
+
+// S^T of one key tile: 4 sub-tiles of 32 keys, k-step major so that the two
+// products into one accumulator are three instructions apart.
+template <int D>
+__device__ __forceinline__ void qk_tile(const Ctx<D>& c, const uint8_t* kb, v16f (&s)[4]) {
+  constexpr int KD = D / 64;
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* kr = kb + t * 32 * D;
+      const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][1]));
+      s[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : s[t]);
+    }
+}
+
+// Keys at or past `valid` (ragged last tile) -> -inf: dropped from the max,
+// probability 0 / code 0.
+// The lane's key offset 4 hh is folded into the bound, so each test compares
+// an immediate with one per-lane value (nothing loop-invariant to hoist).
+__device__ __forceinline__ void mask_tile(v16f (&s)[4], int valid, int hh) {
+  const int lim = valid - 4 * hh;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * t + 8 * (r >> 2) + (r & 3) >= lim) s[t][r] = -INFINITY;
+}
+
+__device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
+  return __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+// E4M3 probability codes of 4 scores of one lane: the dword w of sub-tile t
+// of the B operand of PV.
+template <bool EXPCAST>
+__device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bias, float c8) {
+  if (!EXPCAST) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 0], cj, bias));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 1], cj, bias));
+    const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 2], cj, bias));
+    const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 3], cj, bias));
+    // the high half is written next, so the low write may keep any upper
+    // bits: reuse p0's register instead of a zeroed one
+    uint32_t pk = cvt_pk_e4m3<false>(p0, p1, __float_as_uint(p0));
+    return static_cast<int>(cvt_pk_e4m3<true>(p2, p3, pk));
+  }
+  uint32_t pk = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float code = __builtin_rintf(__builtin_fmaf(s[4 * w + e], c8, bias));
+    code = code < 8.0f ? 0.0f : __builtin_fminf(code, 126.0f);
+    pk |= static_cast<uint32_t>(code) << (8 * e);
+  }
+  return static_cast<int>(pk);
+}
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One step of the recurrence for key tile j, software-pipelined one tile
+// ahead, with the instruction order fixed by hand (scheduling fences):
+//   phase A: the QK products of tile j + 1, each followed by a share of tile
+//            j's probability work (exp2 and E4M3 packing), so the vector ALU
+//            runs while the matrix core works;
+//   phase B: tile j's row sums, PV products and mean restore, each followed
+//            by a share of tile j + 1's max.
+//   kread : K of tile j + 1 (ready)    kwrite: K of tile j + 2 (filled here)
+//   vread : V of tile j (ready)        vwrite: V of tile j + 1 (filled here)
+// Past the last tile the QK product reads a stale buffer; its result is
+// never used.
+template <int D, bool EXPCAST, int VMEAN>
+__device__ __forceinline__ void attn_step(const int j, const Ctx<D>& c, State<D>& st,
+                                          const uint8_t* kread, uint8_t* kwrite,
+                                          const uint8_t* vread, uint8_t* vwrite,
+                                          const float* muread, float* muwrite) {
+  constexpr int KD = D / 64, DT = D / 32;
+  constexpr int NQK = 4 * KD;                // QK products per tile
+  constexpr int GPM = 16 / NQK;              // probability dwords per QK product
+  if (j + 2 < c.nb) issue_k<D>(c, j + 2, kwrite);
+  if (j + 1 < c.nb) issue_v<D, VMEAN>(c, j + 1, vwrite, muwrite);
+
+  const float cj = (c.sq * c.ksc[j]) * c.c_log2;
+  const float m_new = __builtin_fmaxf(st.m, st.mx * cj);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[t][r] *= alpha;
+  }
+  const float bias = EXPCAST ? kExpcastK0 - 8.0f * m_new : 8.0f - m_new;
+  const float c8 = 8.0f * cj;
+
+  // ---- phase A: QK of tile j + 1 (sub-tile major)  ||  P of tile j ----
+  v16f sn[4];
+  v8i pb[2];
+  v8i kf = make_v8i(lds_read16(kread + c.k_rd[0][0]), lds_read16(kread + c.k_rd[0][1]));
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    const int t = i / KD, kd = i % KD;
+    const v8i a = kf;
+    if (i + 1 < NQK) {
+      const int tn = (i + 1) / KD, kdn = (i + 1) % KD;
+      const uint8_t* kr = kread + tn * 32 * D;
+      kf = make_v8i(lds_read16(kr + c.k_rd[kdn][0]), lds_read16(kr + c.k_rd[kdn][1]));
+    }
+    sn[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : sn[t]);
+#pragma unroll
+    for (int g = 0; g < GPM; ++g) {
+      const int q = i * GPM + g, tp = q >> 2, w = q & 3;
+      pb[tp >> 1][4 * (tp & 1) + w] = p_codes4<EXPCAST>(st.s[tp], w, cj, bias, c8);
+    }
+    sched_fence();
+  }
+
+  // ---- phase B: row sums, PV and restore of tile j  ||  max of tile j + 1 ----
+  // row sums on the matrix core: the P codes against an all-ones operand;
+  // every accumulator row holds the lane's query summed over the tile's 128
+  // keys (both lane halves)
+  v16f rs = mfma_fp8(c.ones, pb[0], v16f{});
+  rs = mfma_fp8(c.ones, pb[1], rs);
+  // E8M0 byte of the V block scale (a normal power of two: its exponent
+  // field), and 2^-8 for P's prescale
+  const int sv_e8 = (__float_as_int(c.vsc[j]) >> 23) & 0xFF;
+  float mx = -INFINITY;
+  v8i vf = make_v8i(lds_read16(vread + c.v_rd[0][0]), lds_read16(vread + c.v_rd[0][1]));
+  sched_fence();
+#pragma unroll
+  for (int i = 0; i < 2 * DT; ++i) {
+    const int kk = i / DT, t = i % DT;
+    const v8i a = vf;
+    if (i + 1 < 2 * DT) {
+      const int kkn = (i + 1) / DT, tn = (i + 1) % DT;
+      const uint8_t* vr = vread + tn * 32 * kBlock;
+      vf = make_v8i(lds_read16(vr + c.v_rd[kkn][0]), lds_read16(vr + c.v_rd[kkn][1]));
+    }
+    st.acc[t] = mfma_fp8_scaled(a, pb[kk], st.acc[t], sv_e8, 127 - 8);
+    // a share of the max over sn (64 values per lane, 2 DT shares)
+    constexpr int PER = 64 / (2 * DT);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int q = i * PER + e;
+      mx = __builtin_fmaxf(mx, sn[q >> 4][q & 15]);
+    }
+    sched_fence();
+  }
+  const float ell = rs[0] * (1.0f / 256.0f);
+  if (VMEAN == VS_VMEAN_BLOCK) {
+    // + mu_j (x) l_j, one outer-product instruction per pair of channel
+    // tiles: lanes 0-31 carry mu of tile 2pr, lanes 32-63 of tile 2pr + 1
+#pragma unroll
+    for (int pr = 0; pr < DT / 2; ++pr) {
+      const float mu = muread[64 * pr + c.lane];
+      v32f c2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        c2[r] = st.acc[2 * pr][r];
+        c2[16 + r] = st.acc[2 * pr + 1][r];
+      }
+      c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.acc[2 * pr][r] = c2[r];
+        st.acc[2 * pr + 1][r] = c2[16 + r];
+      }
+    }
+  }
+  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // tile j + 1 is the ragged last tile: mask its padding keys and retake
+  // the max (once per workgroup, outside the interleaved phases)
+  if (j + 2 == c.nb && (c.S & (kBlock - 1))) {
+    mask_tile(sn, c.S - (j + 1) * kBlock, c.hh);
+    mx = tile_max(sn);
+  }
+  st.mx = mx;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.s[t] = sn[t];
+  st.l = alpha * st.l + ell;
+  st.m = m_new;
+
+  // the prefetched tiles are complete and visible to every wave; every wave
+  // is done with the buffers the next step overwrites
+  if (j + 1 < c.nb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
 template <int D, bool EXPCAST, int VMEAN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
@@ -106,10 +354,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
   constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
   constexpr int KRC = D / 16;                // 16-byte chunks per K row
-  constexpr int NDMA = TB / 16 / 64 / 4;     // DMA instructions per wave, tile and tensor
-  __shared__ __attribute__((aligned(1024))) uint8_t sk[2][TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv[2][TB];
-  __shared__ __attribute__((aligned(16))) float smu[2][D];
+  // separate variables per buffer: the compiler then knows a DMA into one
+  // buffer does not alias reads of the other and does not wait for it
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[TB];
+  __shared__ __attribute__((aligned(16))) float smu0[D];
+  __shared__ __attribute__((aligned(16))) float smu1[D];
 
   // ---- workgroup -> (b, h, query block), XCD-contiguous ----
   int qb, h, b;
@@ -125,204 +377,79 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     b = bh_l / H;
   }
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t S_pad = static_cast<size_t>(nb) * kBlock;
 
+  Ctx<D> c;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.lane = lane;
+  c.hh = hh;
+  c.nb = nb;
+  c.S = S;
+  c.c_log2 = c_log2;
   // this lane's query and its B operand (32 bytes per k-step)
-  const int qrow = qb * kBlock + wave * 32 + l32;
-  v8i qa[KD];
+  const int qrow = qb * kBlock + c.wave * 32 + l32;
   {
     const uint8_t* qp = q8 + (bh * S_pad + qrow) * D + 32 * hh;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qp + 64 * kd),
-                        *reinterpret_cast<const uint4*>(qp + 64 * kd + 16));
+      c.qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qp + 64 * kd),
+                          *reinterpret_cast<const uint4*>(qp + 64 * kd + 16));
   }
-  const float sq = q_scale[bh * nb + qb];
-
-  const uint8_t* kbase = k8 + bh * S_pad * D;
-  const uint8_t* vbase = v8 + bh * nb * static_cast<size_t>(TB);
-  const float* mubase = (VMEAN == VS_VMEAN_BLOCK) ? v_mean + bh * nb * D : nullptr;
-  const float* ksc = k_scale + bh * nb;
-  const float* vsc = v_scale + bh * nb;
-
-  // per-lane DMA source offsets (bytes inside a 1 KB block; even and odd
-  // blocks) and operand read bases
-  const int k_src[2] = {dma_src_chunk<KRC>(lane, 0) * 16, dma_src_chunk<KRC>(lane, 1) * 16};
-  const int v_src[2] = {dma_src_chunk<8>(lane, 0) * 16, dma_src_chunk<8>(lane, 1) * 16};
-  int k_rd[KD][2], v_rd[2][2];
+  c.sq = q_scale[bh * nb + qb];
+  c.krs = make_rsrc(k8 + bh * S_pad * D, S_pad * D);
+  c.vrs = make_rsrc(v8 + bh * S_pad * D, S_pad * D);
+  c.murs = make_rsrc(VMEAN == VS_VMEAN_BLOCK ? v_mean + bh * nb * D : v_mean,
+                     VMEAN == VS_VMEAN_BLOCK ? nb * D * sizeof(float) : 0);
+  c.ksc = k_scale + bh * nb;
+  c.vsc = v_scale + bh * nb;
+  c.k_src[0] = dma_src_chunk<KRC>(lane, 0) * 16;
+  c.k_src[1] = dma_src_chunk<KRC>(lane, 1) * 16;
+  c.v_src[0] = dma_src_chunk<8>(lane, 0) * 16;
+  c.v_src[1] = dma_src_chunk<8>(lane, 1) * 16;
 #pragma unroll
   for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      k_rd[kd][e] = l32 * D + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
+      c.k_rd[kd][e] = l32 * D + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      v_rd[kk][e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
+      c.v_rd[kk][e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c.ones[i] = 0x38383838;
 
-  float m = -INFINITY, l = 0.0f;
-  v16f acc[DT];
+  State<D> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) st.acc[t][r] = 0.0f;
 
-#define VS_ISSUE_TILE(J, BUF)                                                          \
-  do {                                                                                 \
-    const uint8_t* kg_ = kbase + static_cast<size_t>(J) * TB;                          \
-    const uint8_t* vg_ = vbase + static_cast<size_t>(J) * TB;                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < NDMA; ++i_) {                              \
-      const int base_ = (wave * NDMA + i_) * 1024;                                     \
-      dma16(kg_ + base_ + k_src[i_ & 1], &sk[(BUF)][base_]);                           \
-      dma16(vg_ + base_ + v_src[i_ & 1], &sv[(BUF)][base_]);                           \
-    }                                                                                  \
-    if (VMEAN == VS_VMEAN_BLOCK && wave == 0 && lane < D / 4)                          \
-      dma16(mubase + static_cast<size_t>(J) * D + 4 * lane, &smu[(BUF)][0]);           \
-  } while (0)
-
-  VS_ISSUE_TILE(0, 0);
+  // ---- prologue: K, V of tile 0 and K of tile 1; scores of tile 0 ----
+  issue_k<D>(c, 0, sk0);
+  issue_v<D, VMEAN>(c, 0, sv0, smu0);
+  if (nb > 1) issue_k<D>(c, 1, sk1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  qk_tile<D>(c, sk0, st.s);
+  const bool ragged = (S & (kBlock - 1)) != 0;
+  if (nb == 1 && ragged) mask_tile(st.s, S, hh);
+  st.mx = tile_max(st.s);
+  __syncthreads();   // sk0 is refilled by the first step
 
-  for (int j = 0; j < nb; ++j) {
-    const int buf = j & 1;
-    const bool last = j == nb - 1;
-    if (!last) VS_ISSUE_TILE(j + 1, buf ^ 1);
-    const uint8_t* skb = sk[buf];
-    const uint8_t* svb = sv[buf];
-
-    // ---- S^T = K_j Q^T : 4 sub-tiles of 32 keys ----
-    v16f s[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint8_t* kr = skb + t * 32 * D;
-      s[t] = mfma_fp8(make_v8i(lds_read16(kr + k_rd[0][0]), lds_read16(kr + k_rd[0][1])), qa[0],
-                      v16f{});
-#pragma unroll
-      for (int kd = 1; kd < KD; ++kd)
-        s[t] = mfma_fp8(make_v8i(lds_read16(kr + k_rd[kd][0]), lds_read16(kr + k_rd[kd][1])),
-                        qa[kd], s[t]);
-    }
-    // keys past S (ragged last tile only): -inf drops them from the max and
-    // gives p = 0 / code 0
-    if (last && (S & (kBlock - 1))) {
-      const int valid = S - j * kBlock;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[t][r] = -INFINITY;
-    }
-
-    // ---- running max, once per tile ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float cj = (sq * ksc[j]) * c_log2;
-    const float m_new = __builtin_fmaxf(m, mx * cj);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-
-    // ---- P tile -> E4M3 B operand; tile row sum ----
-    v8i pb[2];
-    float ell = 0.0f;
-    if (!EXPCAST) {
-      const float bias = 8.0f - m_new;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * w + 0], cj, bias));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * w + 1], cj, bias));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * w + 2], cj, bias));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * w + 3], cj, bias));
-          ell += (p0 + p1) + (p2 + p3);
-          uint32_t pk = cvt_pk_e4m3<false>(p0, p1, 0u);
-          pk = cvt_pk_e4m3<true>(p2, p3, pk);
-          pb[t >> 1][4 * (t & 1) + w] = static_cast<int>(pk);
-        }
-      }
-    } else {
-      const float c8 = 8.0f * cj;
-      const float bias = kExpcastK0 - 8.0f * m_new;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t pk = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float code = __builtin_rintf(__builtin_fmaf(s[t][4 * w + e], c8, bias));
-            code = code < 8.0f ? 0.0f : __builtin_fminf(code, 126.0f);
-            pk |= static_cast<uint32_t>(code) << (8 * e);
-          }
-          ell += (__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(pk), 0) +
-                  __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(pk), 1)) +
-                 (__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(pk), 2) +
-                  __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(pk), 3));
-          pb[t >> 1][4 * (t & 1) + w] = static_cast<int>(pk);
-        }
-      }
-    }
-    ell += __shfl_xor(ell, 32, 64);
-    ell *= (1.0f / 256.0f);
-    l = alpha * l + ell;
-
-    // ---- O^T = alpha O^T + 2^e_j 2^-8 (V^T P^T) + mu (x) l ----
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-    }
-    // E8M0 byte of the V block scale 2^e_j (a normal float: its exponent
-    // field), and 2^-8 for P's prescale
-    const int sv_e8 = (__float_as_int(vsc[j]) >> 23) & 0xFF;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const uint8_t* vr = svb + t * 32 * kBlock;
-      acc[t] = mfma_fp8_scaled(make_v8i(lds_read16(vr + v_rd[0][0]), lds_read16(vr + v_rd[0][1])),
-                               pb[0], acc[t], sv_e8, 127 - 8);
-      acc[t] = mfma_fp8_scaled(make_v8i(lds_read16(vr + v_rd[1][0]), lds_read16(vr + v_rd[1][1])),
-                               pb[1], acc[t], sv_e8, 127 - 8);
-    }
-    if (VMEAN == VS_VMEAN_BLOCK) {
-#pragma unroll
-      for (int pr = 0; pr < DT / 2; ++pr) {
-        // lanes 0-31 carry mu of channel tile 2pr, lanes 32-63 of tile 2pr+1
-        const float mu = smu[buf][64 * pr + lane];
-        v32f c2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          c2[r] = acc[2 * pr][r];
-          c2[16 + r] = acc[2 * pr + 1][r];
-        }
-        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc[2 * pr][r] = c2[r];
-          acc[2 * pr + 1][r] = c2[16 + r];
-        }
-      }
-    }
-    m = m_new;
-
-    if (!last) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+  // ---- main loop, two tiles per trip (static buffer roles) ----
+  for (int j = 0; j < nb; j += 2) {
+    attn_step<D, EXPCAST, VMEAN>(j, c, st, sk1, sk0, sv0, sv1, smu0, smu1);
+    if (j + 1 < nb) attn_step<D, EXPCAST, VMEAN>(j + 1, c, st, sk0, sk1, sv1, sv0, smu1, smu0);
   }
-#undef VS_ISSUE_TILE
 
   // ---- epilogue: O = acc / l (+ sequence mean), lse2 = m + log2 l + q_mu ----
   if (qrow < S) {
-    const float inv_l = 1.0f / l;
+    const float inv_l = 1.0f / st.l;
     float* orow = out + ((static_cast<size_t>(b) * S + qrow) * H + h) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -330,10 +457,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * t + 8 * a + 4 * hh;
         float4 o;
-        o.x = acc[t][4 * a + 0] * inv_l;
-        o.y = acc[t][4 * a + 1] * inv_l;
-        o.z = acc[t][4 * a + 2] * inv_l;
-        o.w = acc[t][4 * a + 3] * inv_l;
+        o.x = st.acc[t][4 * a + 0] * inv_l;
+        o.y = st.acc[t][4 * a + 1] * inv_l;
+        o.z = st.acc[t][4 * a + 2] * inv_l;
+        o.w = st.acc[t][4 * a + 3] * inv_l;
         if (VMEAN == VS_VMEAN_SEQ) {
           const float* mu = v_mean + bh * D + d0;
           o.x += mu[0]; o.y += mu[1]; o.z += mu[2]; o.w += mu[3];
@@ -341,7 +468,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         *reinterpret_cast<float4*>(orow + d0) = o;
       }
     if (hh == 0)
-      lse2[bh * S + qrow] = m + __builtin_amdgcn_logf(l) + (q_mu ? q_mu[bh * S + qrow] : 0.0f);
+      lse2[bh * S + qrow] =
+          st.m + __builtin_amdgcn_logf(st.l) + (q_mu ? q_mu[bh * S + qrow] : 0.0f);
   }
 }
 
@@ -387,6 +515,8 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   const int nb = n_blocks(S);
   const long long total = static_cast<long long>(B) * H * nb;
   if (total > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
+  // one head's codes are addressed through a 32-bit buffer range
+  if (static_cast<long long>(nb) * kBlock * D > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
 
   const float c = softmax_scale * 1.44269504088896341f;
   hipStream_t st = as_stream(stream);

@@ -153,9 +153,12 @@ int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
  *                 (uncentred) logits: m + log2(l) + q_mu.
  * Non-causal full attention; keys past S are masked.  Per 128-key tile:
  * running max m' once per tile; P = E4M3(2^(s - m' + 8)) from an FP32
- * exp2 (l sums the FP32 p), or with VS_EXPCAST the code
- * rint(8 (s - m') + K0), K0 = 120 - 4 (log2(1.5) - 1/2), codes < 8 -> 0
- * (l sums the decoded codes); O accumulates s_V * P.R~ + l_tile * mu_block.
+ * exp2, or with VS_EXPCAST the code rint(8 (s - m') + K0),
+ * K0 = 120 - 4 (log2(1.5) - 1/2), codes < 8 -> 0; the tile row sum l_tile
+ * is the sum of those E4M3 probabilities (formed on the FP8 matrix core);
+ * O accumulates s_V * P.R~ + l_tile * mu_block.
+ * S * D (rounded up to whole blocks) must stay below 2^31 per head
+ * (VS_ERR_UNSUPPORTED otherwise).
  */
 int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                     const float* k_scale, const uint8_t* v8,

@@ -28,9 +28,9 @@ recurrence using the row sum the kernel already accumulates").
 
 Probability casts (``pcast``):
 
-* ``"e4m3"``: P~ = E4M3(p * 2^8) * 2^-8 and l_j = sum of the FP32 p before
-  the cast.  Reading: the pages do not fix P's scale; 2^8 is a power of two
-  (exact), maps p = 1 to 256 (code 0x78) and keeps p >= 2^-14 normal.
+* ``"e4m3"``: P~ = E4M3(p * 2^8) * 2^-8.  Reading: the pages do not fix P's
+  scale; 2^8 is a power of two (exact), maps p = 1 to 256 (code 0x78) and
+  keeps p >= 2^-14 normal.
 * ``"expcast"``: ExpCast-FP8 (VC-Attention summary, Key Contribution 2 and
   Methodology): the E4M3 byte is an affine function of log2 of its value, so
   the code is formed from the log-domain score by one multiply-add and one
@@ -41,9 +41,15 @@ Probability casts (``pcast``):
   code = 8 log2(p) + 120 - 8 delta(M), delta(M) = log2(1 + M/8) - M/8 over
   the eight mantissas M; delta ranges over [0, log2(1.5) - 1/2].  The
   "minimax centring of the one residual error term" is sigma = half that
-  range, K0 = 120 - 8 sigma.  rint rounds half to even.  l_j is the sum of
-  the decoded probabilities (no FP32 p exists on this path).
+  range, K0 = 120 - 8 sigma.  rint rounds half to even.
 * ``"none"``: no cast (P~ = p), for the exactness pins.
+
+Row sum (both casts): l_j is the sum of the tile's probabilities as they
+enter PV, the decoded P~ (for ``"none"`` that is the exact p).  Reading: the
+pages restore the mean "from the row sum the online softmax already
+maintains"; summing the same P~ that multiplies V makes the restore exact for
+the quantized probabilities, P~ (V - mu) + mu sum(P~) = P~ V, so block
+demeaning changes nothing but the residual's quantization error.
 
 Precision (``fp32=True``): the pages fix the exponential and K centring at
 FP32 and the operands at E4M3; every quantity that decides a code is formed
@@ -58,6 +64,8 @@ product of the E4M3 codes; exactly, rounded to float32, or, with
     e4m3:    x_t = f32(S_t c_j + f32(8 - m'))      one FMA
              p8_t = f32(2^x_t),  P~ code = E4M3(p8_t)
     expcast: t_t = f32(S_t f32(8 c_j) + f32(K0 - 8 m'))
+    row sum: sum of P~ (with ``qk_codes``, in the matrix core's arithmetic:
+    the tile's P codes in the PV k order against an all-ones operand)
     accumulation of l and acc: float64.
 
 A one-FMA expression is evaluated in float64 (the product of two float32
@@ -171,7 +179,6 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
             t = rnd(S_raw * rnd(8.0 * cj)[:, None] + bias[:, None])
             codes = expcast_codes(t)
             p_tilde = e4m3.decode(codes) * 2.0 ** -8
-            ell = p_tilde.sum(axis=1)
         else:
             x8 = rnd(S_raw * cj[:, None] + rnd(8.0 - m_new)[:, None])
             p8 = rnd(np.exp2(x8))
@@ -183,7 +190,10 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
                 p_tilde = p8 * 2.0 ** -8
             else:
                 raise ValueError(pcast)
-            ell = (p8 * 2.0 ** -8).sum(axis=1)
+        if codes is not None and qk_codes is not None:
+            ell = matrix_core.row_sum_pv_order(codes) * 2.0 ** -8
+        else:
+            ell = p_tilde.sum(axis=1)
         alpha = np.exp2(m - m_new)          # 0 on the first tile (m = -inf)
         l = alpha * l + ell
         acc = alpha[:, None] * acc + float(v_scale[j]) * (p_tilde @ vb[:n])

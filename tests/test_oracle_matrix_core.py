@@ -89,3 +89,17 @@ def test_c_implementation_equals_the_definition():
         a[(a & 0x7F) == 0x7F] = 0x11          # no NaN codes
         b[(b & 0x7F) == 0x7F] = 0x22
         np.testing.assert_array_equal(matrix_core.mfma_fp8_dot_c(a, b), matrix_core.mfma_fp8_dot(a, b))
+
+
+def test_row_sum_in_pv_order_is_exact_for_equal_codes_and_bounded_otherwise():
+    codes = np.full((3, 128), 0x38, dtype=np.uint8)          # 128 ones
+    np.testing.assert_array_equal(matrix_core.row_sum_pv_order(codes), [128.0] * 3)
+    codes = np.zeros((2, 100), dtype=np.uint8)
+    codes[:, 5] = 0x78                                       # one p = 1 (x 2^8)
+    np.testing.assert_array_equal(matrix_core.row_sum_pv_order(codes), [256.0, 256.0])
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 121, (6, 128)).astype(np.uint8)
+    got = matrix_core.row_sum_pv_order(codes)
+    exact = e4m3.decode(codes).sum(axis=1)
+    assert np.all(np.abs(got - exact) <= 16 * 2.0 ** -13 * 256 + 1e-9)
+    assert sorted(matrix_core.PV_TOKEN_ORDER.tolist()) == list(range(128))
