@@ -8,31 +8,32 @@
 // sum.  Output O and log2-LSE as in FastVideo PR #2048 ("Test Results").
 //
 // gfx950 mapping
-//   1-D grid over (batch, head, 128-query block), ordered so that each XCD
-//   (workgroup id mod 8) walks a contiguous range of heads: the K/V of a head
-//   then streams through one XCD's L2 for all its query blocks.
-//   256 threads = 4 waves; a workgroup owns 128 queries (one Q quantization
-//   block, so s_Q is uniform), each wave 32.  Per 128-key tile j:
-//     S^T = K_j Q^T on v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64 channels
-//       from LDS, B = the wave's 32 queries, held in registers for the whole
-//       loop).  A lane owns one query (lane % 32) and 16 keys per 32-key
-//       sub-tile, so the tile max / row sum need one cross-half exchange.
-//     P is formed in registers and packed to E4M3 straight into the B operand
-//       of PV: the accumulator layout of two key sub-tiles is exactly one
-//       64-token k-step of the PV MFMA, given that V is stored in the matching
-//       token order (vs_quantize_residual).  The tile row sum l_j of those
-//       E4M3 probabilities is one more product on the matrix core (the P
-//       codes against an all-ones A operand), which replaces 64 adds, the
-//       ExpCast decode and the cross-half exchange per lane.
-//     O^T: acc = alpha acc (only when some row's max moved), then
-//       acc += 2^e_j 2^-8 V_j^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (A =
-//       32 channels x 64 tokens): the power-of-two V block scale and P's 2^8
-//       are E8M0 operand scales, so the product accumulates straight into acc;
-//       then the rank-one restore acc += mu_j (x) l_j as
-//       v_mfma_f32_32x32x1_2b_f32 outer products (one per pair of channel
-//       tiles) instead of D FMAs per lane.
-//   K and V tiles (16 KB each at D = 128) are double-buffered in LDS and
-//   filled with global_load_lds_dwordx4 (no staging registers): each lane's
+//   1-D grid over (batch, head, pair of 128-query blocks), ordered so that
+//   each XCD (workgroup id mod 8) walks a contiguous range of heads: the K/V
+//   of a head then streams through one XCD's L2 for all its query blocks.
+//   512 threads = 8 waves in two groups of four; group g owns query block
+//   2 pair + g (one Q quantization block, so s_Q is uniform), each wave 32
+//   queries.  Waves w and w + 4 share a SIMD (round-robin placement), and the
+//   groups run a ping-pong one phase apart, separated by workgroup barriers:
+//   while one wave issues its matrix-core phase, the other wave on the SIMD
+//   runs its vector phase.
+//     M(j): S^T = K_j Q^T on v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64
+//       channels from LDS, B = the wave's 32 queries, held in registers for
+//       the whole loop; a lane owns one query (lane % 32) and 16 keys per
+//       32-key sub-tile), then for tile j - 1: the row sum of its E4M3
+//       probabilities (P codes against an all-ones A operand), O^T +=
+//       2^e 2^-8 V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (the
+//       power-of-two V block scale and P's 2^8 are E8M0 operand scales, so
+//       the product accumulates straight into acc), and the rank-one restore
+//       acc += mu (x) l as v_mfma_f32_32x32x1_2b_f32 outer products.
+//     V(j): tile max (one cross-half exchange), running max, O^T rescale
+//       (only when some row's max moved), and P packed to E4M3 straight into
+//       the B operand of PV: the accumulator layout of two key sub-tiles is
+//       exactly one 64-token k-step of the PV MFMA, given that V is stored in
+//       the matching token order (vs_quantize_residual).
+//   K and V tiles (16 KB each at D = 128) are double-buffered in LDS, shared
+//   by all eight waves, and filled by the first group with buffer_load ...
+//   lds (no staging registers, no per-lane address arithmetic): each lane's
 //   16-byte source is chosen so the LDS image is the XOR-swizzled tile, and
 //   the 128-bit operand reads of 16 consecutive rows hit distinct banks
 //   (gfx950's LDS serves a 128-bit read over 64 banks: rows of 128 B need the
@@ -106,35 +107,40 @@ __device__ __forceinline__ void dma16(rsrc_t rs, int voff, int soff, void* dst) 
                                            voff, soff, 0, 0);
 }
 
-// Uniform values and per-lane constants of one workgroup.
+// Uniform values and per-lane constants of one wave.
 template <int D>
 struct Ctx {
   rsrc_t krs, vrs, murs;                 // this head's K codes, V codes, V block means
   const float* ksc;                      // K block scales of this head
   const float* vsc;                      // V block scales of this head
   float sq, c_log2;
-  int nb, S, wave, hh, lane;
+  int nb, S, dma_wave, hh, lane;         // dma_wave: 0-3 in the DMA group, else -1
   int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
   int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
   v8i qa[D / 64];                        // this lane's query, B operand of QK
   v8i ones;                              // E4M3 ones, A operand of the row sums
 };
 
-// Recurrence state of one wave: raw scores of the tile to be processed
-// next, their maximum, the running max / sum and O^T.
+// Recurrence state of one wave: raw scores s of the current key tile, its
+// E4M3 probabilities pb, the running max m, the factor alpha of the last
+// tile (applied to O^T already, to l when that tile's row sum is known), O^T
+// and l.
 template <int D>
 struct State {
   v16f s[4];
+  v8i pb[2];
   v16f acc[D / 32];
-  float mx, m, l;
+  float m, alpha, l;
 };
 
+// K of tile j into dst: 16 KB (D = 128) as 1 KB DMA blocks, a quarter per
+// wave of the DMA group.
 template <int D>
 __device__ __forceinline__ void issue_k(const Ctx<D>& c, int j, uint8_t* dst) {
   constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int base = (c.wave * NDMA + i) * 1024;
+    const int base = (c.dma_wave * NDMA + i) * 1024;
     dma16(c.krs, c.k_src[i & 1], j * TB + base, dst + base);
   }
 }
@@ -144,39 +150,30 @@ __device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, fl
   constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int base = (c.wave * NDMA + i) * 1024;
+    const int base = (c.dma_wave * NDMA + i) * 1024;
     dma16(c.vrs, c.v_src[i & 1], j * TB + base, dst + base);
   }
-  if (VMEAN == VS_VMEAN_BLOCK && c.wave == 0 && c.lane < D / 4)
+  if (VMEAN == VS_VMEAN_BLOCK && c.dma_wave == 0 && c.lane < D / 4)
     dma16(c.murs, 16 * c.lane, j * D * 4, mu_dst);
 }
 
-// S^T of one key tile: 4 sub-tiles of 32 keys, k-step major so that the two
-// products into one accumulator are three instructions apart.
-template <int D>
-__device__ __forceinline__ void qk_tile(const Ctx<D>& c, const uint8_t* kb, v16f (&s)[4]) {
-  constexpr int KD = D / 64;
-#pragma unroll
-  for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint8_t* kr = kb + t * 32 * D;
-      const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][1]));
-      s[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : s[t]);
-    }
-}
-
 // Keys at or past `valid` (ragged last tile) -> -inf: dropped from the max,
-// probability 0 / code 0.
-// The lane's key offset 4 hh is folded into the bound, so each test compares
-// an immediate with one per-lane value (nothing loop-invariant to hoist).
+// probability 0 / code 0.  Written without compares: a key offset K of the
+// lane is masked iff (valid - 4 hh - 1/2 - K) < 0, and min(s, that * inf) is
+// -inf then and s otherwise (the factor is never 0).  Compare masks would
+// each take a 64-bit scalar register pair.
 __device__ __forceinline__ void mask_tile(v16f (&s)[4], int valid, int hh) {
-  const int lim = valid - 4 * hh;
+  float lim = static_cast<float>(valid - 4 * hh) - 0.5f;
+  // opaque to the optimizer: the bound is loop-invariant where this runs
+  // once, and hoisting its 64 products would only occupy registers
+  asm volatile("" : "+v"(lim));
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * t + 8 * (r >> 2) + (r & 3) >= lim) s[t][r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const float key = static_cast<float>(32 * t + 8 * (r >> 2) + (r & 3));
+      s[t][r] = __builtin_fminf(s[t][r], (lim - key) * INFINITY);
+    }
 }
 
 __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
@@ -202,154 +199,134 @@ __device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bi
     uint32_t pk = cvt_pk_e4m3<false>(p0, p1, __float_as_uint(p0));
     return static_cast<int>(cvt_pk_e4m3<true>(p2, p3, pk));
   }
+  // code = rint(8 (s - m') + K0) capped at 126; codes below 8 -> 0 through
+  // a {0, 1} factor clamp(2 code - 15) (code is an integer), no compares;
+  // the byte is packed by a saturating float -> u8 conversion of an integer
   uint32_t pk = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float code = __builtin_rintf(__builtin_fmaf(s[4 * w + e], c8, bias));
-    code = code < 8.0f ? 0.0f : __builtin_fminf(code, 126.0f);
-    pk |= static_cast<uint32_t>(code) << (8 * e);
+    const float code = __builtin_fminf(__builtin_rintf(__builtin_fmaf(s[4 * w + e], c8, bias)), 126.0f);
+    const float keep = __builtin_amdgcn_fmed3f(__builtin_fmaf(code, 2.0f, -15.0f), 0.0f, 1.0f);
+    pk = __builtin_amdgcn_cvt_pk_u8_f32(code * keep, e, pk);
   }
   return static_cast<int>(pk);
 }
 
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// One step of the recurrence for key tile j, software-pipelined one tile
-// ahead, with the instruction order fixed by hand (scheduling fences):
-//   phase A: the QK products of tile j + 1, each followed by a share of tile
-//            j's probability work (exp2 and E4M3 packing), so the vector ALU
-//            runs while the matrix core works;
-//   phase B: tile j's row sums, PV products and mean restore, each followed
-//            by a share of tile j + 1's max.
-//   kread : K of tile j + 1 (ready)    kwrite: K of tile j + 2 (filled here)
-//   vread : V of tile j (ready)        vwrite: V of tile j + 1 (filled here)
-// Past the last tile the QK product reads a stale buffer; its result is
-// never used.
-template <int D, bool EXPCAST, int VMEAN>
-__device__ __forceinline__ void attn_step(const int j, const Ctx<D>& c, State<D>& st,
-                                          const uint8_t* kread, uint8_t* kwrite,
-                                          const uint8_t* vread, uint8_t* vwrite,
-                                          const float* muread, float* muwrite) {
+// Matrix-core phase M(j) of one wave: S^T of key tile j (if j < nb), then
+// for tile j - 1 (if j >= 1) the row sums of its E4M3 probabilities, PV and
+// the rank-one mean restore, and l's update.
+//   kb: K of tile j      vb, mub: V and V mean of tile j - 1
+template <int D, int VMEAN>
+__device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D>& st,
+                                           const uint8_t* kb, const uint8_t* vb,
+                                           const float* mub) {
   constexpr int KD = D / 64, DT = D / 32;
-  constexpr int NQK = 4 * KD;                // QK products per tile
-  constexpr int GPM = 16 / NQK;              // probability dwords per QK product
-  if (j + 2 < c.nb) issue_k<D>(c, j + 2, kwrite);
-  if (j + 1 < c.nb) issue_v<D, VMEAN>(c, j + 1, vwrite, muwrite);
-
-  const float cj = (c.sq * c.ksc[j]) * c.c_log2;
-  const float m_new = __builtin_fmaxf(st.m, st.mx * cj);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  if (__ballot(alpha != 1.0f)) {
+  if (j < c.nb) {
+    // sub-tile major is fine here: the products of other waves fill the gap
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[t][r] *= alpha;
-  }
-  const float bias = EXPCAST ? kExpcastK0 - 8.0f * m_new : 8.0f - m_new;
-  const float c8 = 8.0f * cj;
-
-  // ---- phase A: QK of tile j + 1 (sub-tile major)  ||  P of tile j ----
-  v16f sn[4];
-  v8i pb[2];
-  v8i kf = make_v8i(lds_read16(kread + c.k_rd[0][0]), lds_read16(kread + c.k_rd[0][1]));
-#pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    const int t = i / KD, kd = i % KD;
-    const v8i a = kf;
-    if (i + 1 < NQK) {
-      const int tn = (i + 1) / KD, kdn = (i + 1) % KD;
-      const uint8_t* kr = kread + tn * 32 * D;
-      kf = make_v8i(lds_read16(kr + c.k_rd[kdn][0]), lds_read16(kr + c.k_rd[kdn][1]));
-    }
-    sn[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : sn[t]);
-#pragma unroll
-    for (int g = 0; g < GPM; ++g) {
-      const int q = i * GPM + g, tp = q >> 2, w = q & 3;
-      pb[tp >> 1][4 * (tp & 1) + w] = p_codes4<EXPCAST>(st.s[tp], w, cj, bias, c8);
-    }
-    sched_fence();
-  }
-
-  // ---- phase B: row sums, PV and restore of tile j  ||  max of tile j + 1 ----
-  // row sums on the matrix core: the P codes against an all-ones operand;
-  // every accumulator row holds the lane's query summed over the tile's 128
-  // keys (both lane halves)
-  v16f rs = mfma_fp8(c.ones, pb[0], v16f{});
-  rs = mfma_fp8(c.ones, pb[1], rs);
-  // E8M0 byte of the V block scale (a normal power of two: its exponent
-  // field), and 2^-8 for P's prescale
-  const int sv_e8 = (__float_as_int(c.vsc[j]) >> 23) & 0xFF;
-  float mx = -INFINITY;
-  v8i vf = make_v8i(lds_read16(vread + c.v_rd[0][0]), lds_read16(vread + c.v_rd[0][1]));
-  sched_fence();
-#pragma unroll
-  for (int i = 0; i < 2 * DT; ++i) {
-    const int kk = i / DT, t = i % DT;
-    const v8i a = vf;
-    if (i + 1 < 2 * DT) {
-      const int kkn = (i + 1) / DT, tn = (i + 1) % DT;
-      const uint8_t* vr = vread + tn * 32 * kBlock;
-      vf = make_v8i(lds_read16(vr + c.v_rd[kkn][0]), lds_read16(vr + c.v_rd[kkn][1]));
-    }
-    st.acc[t] = mfma_fp8_scaled(a, pb[kk], st.acc[t], sv_e8, 127 - 8);
-    // a share of the max over sn (64 values per lane, 2 DT shares)
-    constexpr int PER = 64 / (2 * DT);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int q = i * PER + e;
-      mx = __builtin_fmaxf(mx, sn[q >> 4][q & 15]);
-    }
-    sched_fence();
-  }
-  const float ell = rs[0] * (1.0f / 256.0f);
-  if (VMEAN == VS_VMEAN_BLOCK) {
-    // + mu_j (x) l_j, one outer-product instruction per pair of channel
-    // tiles: lanes 0-31 carry mu of tile 2pr, lanes 32-63 of tile 2pr + 1
-#pragma unroll
-    for (int pr = 0; pr < DT / 2; ++pr) {
-      const float mu = muread[64 * pr + c.lane];
-      v32f c2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        c2[r] = st.acc[2 * pr][r];
-        c2[16 + r] = st.acc[2 * pr + 1][r];
+      for (int t = 0; t < 4; ++t) {
+        const uint8_t* kr = kb + t * 32 * D;
+        const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][1]));
+        st.s[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : st.s[t]);
       }
-      c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
+  }
+  if (j >= 1) {
+    // row sums: P codes against E4M3 ones; every accumulator row holds the
+    // lane's query summed over the tile's 128 keys (both lane halves)
+    v16f rs = mfma_fp8(c.ones, st.pb[0], v16f{});
+    rs = mfma_fp8(c.ones, st.pb[1], rs);
+    // O^T += 2^e 2^-8 V^T P^T: the E8M0 byte of the V block scale (a normal
+    // power of two: its exponent field) and 2^-8 for P's prescale
+    const int sv_e8 = (__float_as_int(c.vsc[j - 1]) >> 23) & 0xFF;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        st.acc[2 * pr][r] = c2[r];
-        st.acc[2 * pr + 1][r] = c2[16 + r];
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const uint8_t* vr = vb + t * 32 * kBlock;
+        const v8i a = make_v8i(lds_read16(vr + c.v_rd[kk][0]), lds_read16(vr + c.v_rd[kk][1]));
+        st.acc[t] = mfma_fp8_scaled(a, st.pb[kk], st.acc[t], sv_e8, 127 - 8);
+      }
+    const float ell = rs[0] * (1.0f / 256.0f);
+    if (VMEAN == VS_VMEAN_BLOCK) {
+      // + mu (x) l, one outer product per pair of channel tiles: lanes 0-31
+      // carry mu of tile 2pr, lanes 32-63 of tile 2pr + 1
+#pragma unroll
+      for (int pr = 0; pr < DT / 2; ++pr) {
+        const float mu = mub[64 * pr + c.lane];
+        v32f c2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          c2[r] = st.acc[2 * pr][r];
+          c2[16 + r] = st.acc[2 * pr + 1][r];
+        }
+        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st.acc[2 * pr][r] = c2[r];
+          st.acc[2 * pr + 1][r] = c2[16 + r];
+        }
       }
     }
-  }
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // tile j + 1 is the ragged last tile: mask its padding keys and retake
-  // the max (once per workgroup, outside the interleaved phases)
-  if (j + 2 == c.nb && (c.S & (kBlock - 1))) {
-    mask_tile(sn, c.S - (j + 1) * kBlock, c.hh);
-    mx = tile_max(sn);
-  }
-  st.mx = mx;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) st.s[t] = sn[t];
-  st.l = alpha * st.l + ell;
-  st.m = m_new;
-
-  // the prefetched tiles are complete and visible to every wave; every wave
-  // is done with the buffers the next step overwrites
-  if (j + 1 < c.nb) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    st.l = st.alpha * st.l + ell;
   }
 }
 
+// Vector phase V(j) of one wave, j < nb: mask (ragged last tile), tile max,
+// running max, O^T rescale, E4M3 probabilities of key tile j.
+template <int D, bool EXPCAST>
+__device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D>& st) {
+  constexpr int DT = D / 32;
+  if (j == c.nb - 1 && (c.S & (kBlock - 1))) mask_tile(st.s, c.S - j * kBlock, c.hh);
+  const float cj = (c.sq * c.ksc[j]) * c.c_log2;
+  const float m_new = __builtin_fmaxf(st.m, tile_max(st.s) * cj);
+  st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  if (__ballot(st.alpha != 1.0f)) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[t][r] *= st.alpha;
+  }
+  st.m = m_new;
+  const float bias = EXPCAST ? kExpcastK0 - 8.0f * m_new : 8.0f - m_new;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    st.pb[q >> 3][q & 7] = p_codes4<EXPCAST>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+}
+
+// One trip of the ping-pong: M(j), barrier, V(j), barrier.  The two wave
+// groups run it one phase apart, so on every SIMD one wave's matrix-core
+// phase overlaps the other wave's vector phase.  The DMA group issues the
+// copies of K tile j + 1 and V tile j at the start of its M(j) and waits for
+// them before the barrier that ends its V(j); the buffers it overwrites were
+// last read in the other group's M(j - 1), which ended at the barrier before.
+//   kb: K_j (read)     kw: K_{j+1} (filled)
+//   vb: V_{j-1} (read) vw: V_j (filled)
 template <int D, bool EXPCAST, int VMEAN>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D>& c, State<D>& st,
+                                              const uint8_t* kb, uint8_t* kw,
+                                              const uint8_t* vb, uint8_t* vw,
+                                              const float* mub, float* muw) {
+  if (c.dma_wave >= 0 && j < c.nb) {
+    if (j + 1 < c.nb) issue_k<D>(c, j + 1, kw);
+    issue_v<D, VMEAN>(c, j, vw, muw);
+  }
+  phase_mfma<D, VMEAN>(j, c, st, kb, vb, mub);
+  __syncthreads();
+  if (j < c.nb) phase_valu<D, EXPCAST>(j, c, st);
+  if (c.dma_wave >= 0) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+template <int D, bool EXPCAST, int VMEAN>
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, const float* __restrict__ q_mu, int S, int H,
-    int nb, int total, float c_log2, float* __restrict__ out, float* __restrict__ lse2) {
+    int nb, int npairs, int total, float c_log2, float* __restrict__ out,
+    float* __restrict__ lse2) {
   constexpr int KD = D / 64;                 // k-steps of the QK product
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
   constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
@@ -363,39 +340,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) float smu0[D];
   __shared__ __attribute__((aligned(16))) float smu1[D];
 
-  // ---- workgroup -> (b, h, query block), XCD-contiguous ----
-  int qb, h, b;
+  // ---- workgroup -> (b, h, pair of query blocks), XCD-contiguous ----
+  int qp, h, b;
   {
     const int L = blockIdx.x;
     const int xcd = L & 7, idx = L >> 3;
     const int per = total >> 3, rem = total & 7;
     const int logical = xcd < rem ? xcd * (per + 1) + idx
                                   : rem * (per + 1) + (xcd - rem) * per + idx;
-    qb = logical % nb;
-    const int bh_l = logical / nb;
+    qp = logical % npairs;
+    const int bh_l = logical / npairs;
     h = bh_l % H;
     b = bh_l / H;
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;               // waves w and w + 4 share a SIMD
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t S_pad = static_cast<size_t>(nb) * kBlock;
+  // group g owns query block 2 qp + g; past the last block (odd nb) it runs
+  // on a copy of the last block and writes nothing
+  const int qb_raw = 2 * qp + group;
+  const int qb = qb_raw < nb ? qb_raw : nb - 1;
 
   Ctx<D> c;
-  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.dma_wave = group == 0 ? wave : -1;
   c.lane = lane;
   c.hh = hh;
   c.nb = nb;
   c.S = S;
   c.c_log2 = c_log2;
-  // this lane's query and its B operand (32 bytes per k-step)
-  const int qrow = qb * kBlock + c.wave * 32 + l32;
+  const int qrow = qb * kBlock + (wave & 3) * 32 + l32;
   {
-    const uint8_t* qp = q8 + (bh * S_pad + qrow) * D + 32 * hh;
+    const uint8_t* qptr = q8 + (bh * S_pad + qrow) * D + 32 * hh;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      c.qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qp + 64 * kd),
-                          *reinterpret_cast<const uint4*>(qp + 64 * kd + 16));
+      c.qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qptr + 64 * kd),
+                          *reinterpret_cast<const uint4*>(qptr + 64 * kd + 16));
   }
   c.sq = q_scale[bh * nb + qb];
   c.krs = make_rsrc(k8 + bh * S_pad * D, S_pad * D);
@@ -424,31 +406,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   State<D> st;
   st.m = -INFINITY;
   st.l = 0.0f;
+  st.alpha = 1.0f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[t][r] = 0.0f;
 
-  // ---- prologue: K, V of tile 0 and K of tile 1; scores of tile 0 ----
-  issue_k<D>(c, 0, sk0);
-  issue_v<D, VMEAN>(c, 0, sv0, smu0);
-  if (nb > 1) issue_k<D>(c, 1, sk1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  qk_tile<D>(c, sk0, st.s);
-  const bool ragged = (S & (kBlock - 1)) != 0;
-  if (nb == 1 && ragged) mask_tile(st.s, S, hh);
-  st.mx = tile_max(st.s);
-  __syncthreads();   // sk0 is refilled by the first step
-
-  // ---- main loop, two tiles per trip (static buffer roles) ----
-  for (int j = 0; j < nb; j += 2) {
-    attn_step<D, EXPCAST, VMEAN>(j, c, st, sk1, sk0, sv0, sv1, smu0, smu1);
-    if (j + 1 < nb) attn_step<D, EXPCAST, VMEAN>(j + 1, c, st, sk0, sk1, sv1, sv0, smu1, smu0);
+  // ---- prologue: K of tile 0; group 1 runs one phase behind group 0 ----
+  if (c.dma_wave >= 0) {
+    issue_k<D>(c, 0, sk0);
+    __builtin_amdgcn_s_waitcnt(0);
   }
+  __syncthreads();
+  if (group == 1) __syncthreads();
+
+  // ---- nb + 1 trips, two per loop iteration (static buffer roles) ----
+  for (int j = 0; j <= nb; j += 2) {
+    pingpong_trip<D, EXPCAST, VMEAN>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0);
+    if (j + 1 <= nb)
+      pingpong_trip<D, EXPCAST, VMEAN>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0, smu1);
+  }
+  if (group == 0) __syncthreads();
 
   // ---- epilogue: O = acc / l (+ sequence mean), lse2 = m + log2 l + q_mu ----
-  if (qrow < S) {
+  if (qb_raw < nb && qrow < S) {
     const float inv_l = 1.0f / st.l;
     float* orow = out + ((static_cast<size_t>(b) * S + qrow) * H + h) * D;
 #pragma unroll
@@ -476,18 +457,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 template <int D, bool EXPCAST>
 void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
                const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
-               const float* vm, const float* qmu, int S, int H, int nb, float c, float* out,
-               float* lse2) {
-  const dim3 grid(total), block(256);
+               const float* vm, const float* qmu, int S, int H, int nb, int npairs, float c,
+               float* out, float* lse2) {
+  const dim3 grid(total), block(512);
   if (vmean_mode == VS_VMEAN_BLOCK)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
   else if (vmean_mode == VS_VMEAN_SEQ)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
 }
 
 }  // namespace
@@ -513,7 +494,9 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
   const int nb = n_blocks(S);
-  const long long total = static_cast<long long>(B) * H * nb;
+  // one workgroup per (batch, head, pair of 128-query blocks)
+  const int npairs = (nb + 1) / 2;
+  const long long total = static_cast<long long>(B) * H * npairs;
   if (total > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
   // one head's codes are addressed through a 32-bit buffer range
   if (static_cast<long long>(nb) * kBlock * D > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
@@ -523,11 +506,11 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   const bool ec = (flags & VS_EXPCAST) != 0;
   const int tot = static_cast<int>(total);
   if (D == 128) {
-    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
-    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
+    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
   } else {
-    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
-    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, c, out, lse2);
+    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
+    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
   }
   return launch_status();
 }
