@@ -25,6 +25,28 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8 smoothed-attn TFLOP/s (4·S²·D·H) and % FP8 MFMA peak, S=32626 H=56 D=128"
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_live_traffic.json")
+
+
+def _traffic(workload, expcast):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    record (FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB copy), or None when the
+    record is for another workload or the kernel sources changed since."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        if rec.get("workload") != workload or expcast:
+            return None
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _cpu_baseline(w, q, k, v, rows_n):
@@ -60,7 +82,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="live")
     ap.add_argument("--expcast", type=int, default=None, help="override the workload's ExpCast flag")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a known-size "
@@ -143,7 +165,8 @@ def main():
                    "prep_ms": round(ms_step - attn_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": _traffic(w.name, expcast)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
