@@ -176,13 +176,23 @@ __device__ __forceinline__ void mask_tile(v16f (&s)[4], int valid, int hh) {
     }
 }
 
+// Max of x over lanes l and l ^ 32 without an LDS round trip:
+// v_permlane32_swap of two copies of x leaves the other half's value of
+// every lane in one of the two results (lanes 0-31 in the second, lanes
+// 32-63 in the first), and x itself in the other.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __builtin_fmaxf(x, __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
-  return __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+  return max_with_other_half(mx);
 }
 
 // E4M3 probability codes of 4 scores of one lane: the dword w of sub-tile t
@@ -270,6 +280,12 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
       }
     }
     st.l = st.alpha * st.l + ell;
+    // keep the products in this phase: left to itself the compiler may sink
+    // them past the barrier, up to the vector phase's rescale, which then
+    // reads their results a few instructions after issue (seen to give wrong
+    // O without the mean restore, which otherwise pins them)
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(st.acc[t]));
   }
 }
 
