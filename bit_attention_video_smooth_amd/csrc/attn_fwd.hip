@@ -131,6 +131,10 @@ struct State {
   v8i pb[2];
   v16f acc[D / 32];
   float m, alpha, l;
+  // block scales one tile ahead of their use (scalar loads complete while a
+  // whole phase runs): K scale of the next V phase's tile, V scale of the
+  // next M phase's PV tile
+  float ks, vs;
 };
 
 // K of tile j into dst: 16 KB (D = 128) as 1 KB DMA blocks, a quarter per
@@ -249,7 +253,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
     rs = mfma_fp8(c.ones, st.pb[1], rs);
     // O^T += 2^e 2^-8 V^T P^T: the E8M0 byte of the V block scale (a normal
     // power of two: its exponent field) and 2^-8 for P's prescale
-    const int sv_e8 = (__float_as_int(c.vsc[j - 1]) >> 23) & 0xFF;
+    const int sv_e8 = (__float_as_int(st.vs) >> 23) & 0xFF;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -286,6 +290,8 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
     // O without the mean restore, which otherwise pins them)
 #pragma unroll
     for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(st.acc[t]));
+    // after the last LDS read of the phase, so no wait joins the two
+    st.vs = c.vsc[j < c.nb ? j : c.nb - 1];
   }
 }
 
@@ -295,7 +301,7 @@ template <int D, bool EXPCAST>
 __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D>& st) {
   constexpr int DT = D / 32;
   if (j == c.nb - 1 && (c.S & (kBlock - 1))) mask_tile(st.s, c.S - j * kBlock, c.hh);
-  const float cj = (c.sq * c.ksc[j]) * c.c_log2;
+  const float cj = (c.sq * st.ks) * c.c_log2;
   const float m_new = __builtin_fmaxf(st.m, tile_max(st.s) * cj);
   st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   if (__ballot(st.alpha != 1.0f)) {
@@ -309,6 +315,7 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D
 #pragma unroll
   for (int q = 0; q < 16; ++q)
     st.pb[q >> 3][q & 7] = p_codes4<EXPCAST>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+  st.ks = c.ksc[j + 1 < c.nb ? j + 1 : j];
 }
 
 // One trip of the ping-pong: M(j), barrier, V(j), barrier.  The two wave
@@ -420,6 +427,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   for (int i = 0; i < 8; ++i) c.ones[i] = 0x38383838;
 
   State<D> st;
+  st.ks = c.ksc[0];
+  st.vs = c.vsc[0];
   st.m = -INFINITY;
   st.l = 0.0f;
   st.alpha = 1.0f;
