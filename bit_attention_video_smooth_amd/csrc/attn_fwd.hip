@@ -201,7 +201,7 @@ __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
 
 // E4M3 probability codes of 4 scores of one lane: the dword w of sub-tile t
 // of the B operand of PV.
-template <bool EXPCAST>
+template <bool EXPCAST, bool CAP>
 __device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bias, float c8) {
   if (!EXPCAST) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 0], cj, bias));
@@ -213,17 +213,21 @@ __device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bi
     uint32_t pk = cvt_pk_e4m3<false>(p0, p1, __float_as_uint(p0));
     return static_cast<int>(cvt_pk_e4m3<true>(p2, p3, pk));
   }
-  // code = rint(8 (s - m') + K0) capped at 126; codes below 8 -> 0 through
-  // a {0, 1} factor clamp(2 code - 15) (code is an integer), no compares;
-  // the byte is packed by a saturating float -> u8 conversion of an integer
+  // ExpCast: code = rint(8 (s - m') + K0), capped at 126, codes below 8 -> 0.
+  // v_cvt_pk_u8_f32 rounds half to even and saturates at 0 (so negative
+  // pre-codes and -inf of masked keys give 0) while packing the byte.  The
+  // cap only binds when |m'| is huge (CAP, a uniform slow path); otherwise
+  // every byte is <= 121, so b + 0x78 carries into bit 7 exactly when b >= 8,
+  // and the mask 0x80 - 0x01 = 0x7F keeps those bytes and clears the rest.
   uint32_t pk = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float code = __builtin_fminf(__builtin_rintf(__builtin_fmaf(s[4 * w + e], c8, bias)), 126.0f);
-    const float keep = __builtin_amdgcn_fmed3f(__builtin_fmaf(code, 2.0f, -15.0f), 0.0f, 1.0f);
-    pk = __builtin_amdgcn_cvt_pk_u8_f32(code * keep, e, pk);
+    float x = __builtin_fmaf(s[4 * w + e], c8, bias);
+    if (CAP) x = __builtin_fminf(x, 126.0f);
+    pk = __builtin_amdgcn_cvt_pk_u8_f32(x, e, pk);
   }
-  return static_cast<int>(pk);
+  const uint32_t m = (pk + 0x78787878u) & 0x80808080u;
+  return static_cast<int>(pk & (m - (m >> 7)));
 }
 
 // Matrix-core phase M(j) of one wave: S^T of key tile j (if j < nb), then
@@ -254,14 +258,20 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
     // O^T += 2^e 2^-8 V^T P^T: the E8M0 byte of the V block scale (a normal
     // power of two: its exponent field) and 2^-8 for P's prescale
     const int sv_e8 = (__float_as_int(st.vs) >> 23) & 0xFF;
+    // V fragments read one product ahead (the fence keeps each read above
+    // the product before it)
+    auto vfrag = [&](int i) {
+      const uint8_t* vr = vb + (i % DT) * 32 * kBlock;
+      return make_v8i(lds_read16(vr + c.v_rd[i / DT][0]), lds_read16(vr + c.v_rd[i / DT][1]));
+    };
+    v8i vf = vfrag(0);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const uint8_t* vr = vb + t * 32 * kBlock;
-        const v8i a = make_v8i(lds_read16(vr + c.v_rd[kk][0]), lds_read16(vr + c.v_rd[kk][1]));
-        st.acc[t] = mfma_fp8_scaled(a, st.pb[kk], st.acc[t], sv_e8, 127 - 8);
-      }
+    for (int i = 0; i < 2 * DT; ++i) {
+      const v8i a = vf;
+      if (i + 1 < 2 * DT) vf = vfrag(i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      st.acc[i % DT] = mfma_fp8_scaled(a, st.pb[i / DT], st.acc[i % DT], sv_e8, 127 - 8);
+    }
     const float ell = rs[0] * (1.0f / 256.0f);
     if (VMEAN == VS_VMEAN_BLOCK) {
       // + mu (x) l, one outer product per pair of channel tiles: lanes 0-31
@@ -312,9 +322,17 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D
   }
   st.m = m_new;
   const float bias = EXPCAST ? kExpcastK0 - 8.0f * m_new : 8.0f - m_new;
+  // ExpCast pre-codes stay below 126.5 unless rounding of 8 m' is coarse
+  // (|m'| >= 2^20 log2 units): only then is the cap applied per element
+  if (EXPCAST && __ballot(__builtin_fabsf(m_new) >= 1048576.0f)) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    st.pb[q >> 3][q & 7] = p_codes4<EXPCAST>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+    for (int q = 0; q < 16; ++q)
+      st.pb[q >> 3][q & 7] = p_codes4<true, true>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      st.pb[q >> 3][q & 7] = p_codes4<EXPCAST, false>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+  }
   st.ks = c.ksc[j + 1 < c.nb ? j + 1 : j];
 }
 
