@@ -10,21 +10,24 @@
 // permutation are the same on every run and every implementation:
 //   amax    grid (nb,H,B): per-head max |V| (bf16 magnitude bits, an integer
 //           max, combined with an integer atomic max)
-//   codes   grid (nb,H,B): codes = rint(V * 2^-e) as int8 [B,H,S,D]
+//   codes   grid (nb,H,B): codes = rint(V * 2^-e) as int8 [B,H,S,D], and a
+//           channel-major copy [B,H,D,S32] (S32 = S rounded up to 32, zero
+//           padded) through an LDS transpose, for the member-sum products
 //   init    grid (H,B): centroid j = codes of token floor(j*S/k)
-//   T x { assign grid (ceil(S/256),H,B): one token per thread, distances
-//           |c|^2 - 2 v.c with v_dot4_i32_i8 against centroids broadcast from
-//           LDS, first minimum wins; member sums and counts accumulated in
-//           LDS with integer atomics (order-independent), then added to the
-//           global sums with integer atomics;
-//         update grid (H,B): c = round-half-away(sum/count), empty keeps }
+//   T x { assign grid (ceil(S/2048),H,B): distances |c|^2 - 2 v.c as int8
+//           matrix-core products (centroid tile x 32 tokens, exact int32),
+//           first minimum wins; member sums as a second int8 product,
+//           one-hot(labels) x channel-major codes, reduced over the
+//           workgroup's 2048 tokens and written as one partial per chunk;
+//         update grid (H,B): partials summed in chunk order (deterministic),
+//           c = round-half-away(sum/count), empty clusters keep theirs }
 //   hist    grid (ceil(S/256),H,B): label histogram per 256-token chunk
 //   scan    grid (H,B): per (chunk, label) start offsets of a stable sort
 //   scatter grid (ceil(S/256),H,B): rank among equal labels inside a wave
 //           from ballots, wave counts through LDS -> perm
 //   gather  grid (ceil(S/rows),H,B): K'[i] = K[perm[i]], V'[i] = V[perm[i]]
 // All but the assign pass are HBM-bound copies/reductions; the assign pass is
-// S*k*D int8 MACs per head at 4 MACs per lane-op.
+// 2*S*k*D int8 MACs per head on v_mfma_i32_32x32x32_i8.
 #include <algorithm>
 
 #include "common.h"
@@ -32,22 +35,29 @@
 namespace vs {
 namespace {
 
-constexpr int kChunk = 256;                 // tokens per assign / sort workgroup
+constexpr int kChunk = 256;                 // tokens per sort workgroup
+constexpr int kAsg = 2048;                  // tokens per assign workgroup (4 waves x 16 x 32)
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct KmWs {
   uint32_t* amax;     // [B,H]
   int8_t* codes;      // [B,H,S,D]
+  int8_t* codes_t;    // [B,H,D,S32]
   int8_t* cent;       // [B,H,k,D]
-  int32_t* sums;      // [B,H,k,D]
-  int32_t* cnt;       // [B,H,k]
+  int32_t* psum;      // [B,H,nasg,k,D] partial member sums per assign chunk
+  int32_t* pcnt;      // [B,H,nasg,k] partial member counts per assign chunk
   int32_t* chunk;     // [B,H,nchunk,k]
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+__host__ __device__ inline int round32(int S) { return (S + 31) & ~31; }
 
 size_t km_layout(int B, int S, int H, int D, int k, char* base, KmWs* ws) {
   const size_t bh = static_cast<size_t>(B) * H;
   const size_t nchunk = (static_cast<size_t>(S) + kChunk - 1) / kChunk;
+  const size_t nasg = (static_cast<size_t>(S) + kAsg - 1) / kAsg;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -56,16 +66,18 @@ size_t km_layout(int B, int S, int H, int D, int k, char* base, KmWs* ws) {
   };
   char* a = take(bh * sizeof(uint32_t));
   char* c = take(bh * S * D);
+  char* ct = take(bh * D * static_cast<size_t>(round32(S)));
   char* ce = take(bh * k * D);
-  char* su = take(bh * k * D * sizeof(int32_t));
-  char* cn = take(bh * k * sizeof(int32_t));
+  char* ps = take(bh * nasg * k * D * sizeof(int32_t));
+  char* pc = take(bh * nasg * k * sizeof(int32_t));
   char* ch = take(bh * nchunk * k * sizeof(int32_t));
   if (ws) {
     ws->amax = reinterpret_cast<uint32_t*>(a);
     ws->codes = reinterpret_cast<int8_t*>(c);
+    ws->codes_t = reinterpret_cast<int8_t*>(ct);
     ws->cent = reinterpret_cast<int8_t*>(ce);
-    ws->sums = reinterpret_cast<int32_t*>(su);
-    ws->cnt = reinterpret_cast<int32_t*>(cn);
+    ws->psum = reinterpret_cast<int32_t*>(ps);
+    ws->pcnt = reinterpret_cast<int32_t*>(pc);
     ws->chunk = reinterpret_cast<int32_t*>(ch);
   }
   return off;
@@ -123,19 +135,23 @@ __device__ __forceinline__ int code_exponent(uint32_t amax_bits) {
 template <int D>
 __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restrict__ v, int S,
                                                        int H, const uint32_t* __restrict__ amax,
-                                                       int8_t* __restrict__ codes) {
+                                                       int8_t* __restrict__ codes,
+                                                       int8_t* __restrict__ codes_t) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
+  constexpr int TS = D + 4;                 // LDS row stride (bytes): fewer bank conflicts
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * TS];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
+  const int S32 = round32(S);
   const double sc = ldexp(1.0, -code_exponent(amax[bh]));
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    const int tok = j * kBlock + r + ROWS * i;
+    const int row = r + ROWS * i, tok = j * kBlock + row;
+    uint32_t out[2] = {0u, 0u};
     if (tok < S) {
       const uint4 w = *reinterpret_cast<const uint4*>(v + token_offset(VS_LAYOUT_BSHD, b, tok, h, S, H, D) + 8 * c);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      uint32_t out[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int lo = static_cast<int>(rint(static_cast<double>(bf16_to_f32(ww[e] & 0xFFFFu)) * sc));
@@ -145,125 +161,205 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
       }
       *reinterpret_cast<uint2*>(codes + (bh * S + tok) * D + 8 * c) = make_uint2(out[0], out[1]);
     }
+    // the transposed copy takes zeros for tokens past S
+    *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c) = out[0];
+    *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c + 4) = out[1];
+  }
+  __syncthreads();
+  // channel-major copy: 16-token chunks of one channel, 8 lanes per channel
+  // row (128 contiguous bytes of one row per 8 lanes)
+  for (int q = threadIdx.x; q < D * (kBlock / 16); q += 256) {
+    const int d = q / (kBlock / 16), t0 = 16 * (q % (kBlock / 16));
+    if (j * kBlock + t0 >= S32) continue;
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x |= static_cast<uint32_t>(tile[(t0 + 4 * e + u) * TS + d]) << (8 * u);
+      wv[e] = x;
+    }
+    *reinterpret_cast<uint4*>(codes_t + (bh * D + d) * S32 + j * kBlock + t0) =
+        make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void km_init_kernel(const int8_t* __restrict__ codes, int S,
-                                                      int H, int k, int8_t* __restrict__ cent,
-                                                      int32_t* __restrict__ sums,
-                                                      int32_t* __restrict__ cnt) {
+                                                      int H, int k, int8_t* __restrict__ cent) {
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t bh = static_cast<size_t>(b) * H + h;
   for (int idx = threadIdx.x; idx < k * D; idx += blockDim.x) {
     const int jj = idx / D, d = idx % D;
     const long long src = (static_cast<long long>(jj) * S) / k;
     cent[bh * k * D + idx] = codes[(bh * S + src) * D + d];
-    sums[bh * k * D + idx] = 0;
   }
-  for (int jj = threadIdx.x; jj < k; jj += blockDim.x) cnt[bh * k + jj] = 0;
 }
 
-// One token per thread.  LDS: centroids (int8, k x D), their squared norms,
-// and a slice of member sums (int32) of 4096 entries (16 KB); k above the
-// slice size takes several passes over the slices.
+// Per byte of x: 1 where the byte is zero, else 0 (no carries between
+// bytes: the low seven bits are added separately from the top bit).
+__device__ __forceinline__ uint32_t zero_bytes_to_ones(uint32_t x) {
+  const uint32_t t = (x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+  return (~(t | x | 0x7F7F7F7Fu)) >> 7;
+}
+
+// Assign pass over a chunk of 2048 tokens: 4 waves x 16 blocks of 32 tokens.
+//   labels: dist^T (centroids x tokens) = C X^T on v_mfma_i32_32x32x32_i8, per
+//     32-centroid tile and 32-channel k-step (A = centroid rows from LDS, B =
+//     the block's token codes); a lane holds 16 centroids of one token, the
+//     other 16 in lane ^ 32, so the argmin is a register scan plus one
+//     v_permlane32_swap (ties: lowest index).
+//   sums: S (centroid tile x channels) += onehot(labels) (tile x tokens) *
+//     X (tokens x channels), B = 16 tokens of one channel from the
+//     channel-major codes; the four waves' tiles meet in LDS and one partial
+//     per (chunk, tile) goes to global memory.  Tokens past S have zero codes
+//     there, so their one-hot bytes need no mask.
 template <int D>
-__global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict__ codes, int S,
-                                                        int H, int k,
+__global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict__ codes,
+                                                        const int8_t* __restrict__ codes_t,
+                                                        int S, int H, int k,
                                                         const int8_t* __restrict__ cent,
                                                         int32_t* __restrict__ labels,
-                                                        int32_t* __restrict__ sums,
-                                                        int32_t* __restrict__ cnt) {
-  constexpr int DW = D / 4;                         // int8x4 words per token
-  constexpr int SLICE = 4096 / D;                   // clusters per LDS sum slice
-  __shared__ __attribute__((aligned(16))) int32_t scent[256 * DW];
+                                                        int32_t* __restrict__ psum,
+                                                        int32_t* __restrict__ pcnt) {
+  constexpr int KS = D / 32;                // 32-channel k-steps
+  constexpr int BPW = kAsg / 32 / 4;        // 32-token blocks per wave
+  __shared__ __attribute__((aligned(16))) int8_t scent[256 * D];
   __shared__ int32_t snorm[256];
   __shared__ int32_t scnt[256];
-  __shared__ int32_t ssum[SLICE * D];
-  const int h = blockIdx.y, b = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) uint8_t slab[kAsg];
+  __shared__ int32_t sred[32 * D];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = static_cast<size_t>(b) * H + h;
-  const int tok = blockIdx.x * kChunk + threadIdx.x;
-  const bool valid = tok < S;
+  const int nasg = gridDim.x;
+  const int S32 = round32(S);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntile = (k + 31) / 32;
 
-  const int32_t* gc = reinterpret_cast<const int32_t*>(cent + bh * k * D);
-  for (int i = threadIdx.x; i < k * DW; i += 256) scent[i] = gc[i];
-  for (int i = threadIdx.x; i < k; i += 256) scnt[i] = 0;
+  const int4* gc = reinterpret_cast<const int4*>(cent + bh * k * D);
+  for (int i = threadIdx.x; i < k * D / 16; i += 256) reinterpret_cast<int4*>(scent)[i] = gc[i];
+  for (int i = threadIdx.x; i < 256; i += 256) scnt[i] = 0;
+  for (int i = threadIdx.x; i < 32 * D; i += 256) sred[i] = 0;
   __syncthreads();
   for (int jj = threadIdx.x; jj < k; jj += 256) {
     int n2 = 0;
+    const int32_t* row = reinterpret_cast<const int32_t*>(scent + jj * D);
 #pragma unroll 8
-    for (int i = 0; i < DW; ++i) n2 = __builtin_amdgcn_sdot4(scent[jj * DW + i], scent[jj * DW + i], n2, false);
+    for (int i = 0; i < D / 4; ++i) n2 = __builtin_amdgcn_sdot4(row[i], row[i], n2, false);
     snorm[jj] = n2;
   }
-
-  int32_t x[DW];
-  if (valid) {
-    const int4* src = reinterpret_cast<const int4*>(codes + (bh * S + tok) * D);
-#pragma unroll
-    for (int i = 0; i < DW / 4; ++i) {
-      const int4 w = src[i];
-      x[4 * i] = w.x; x[4 * i + 1] = w.y; x[4 * i + 2] = w.z; x[4 * i + 3] = w.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < DW; ++i) x[i] = 0;
-  }
   __syncthreads();
 
-  int best = 0x7FFFFFFF, lab = 0;
-  for (int jj = 0; jj < k; ++jj) {
-    int dot = 0;
+  // ---- labels ----
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave * BPW + i;
+    const int tb = chunk * kAsg + blk * 32;
+    if (tb >= S) break;
+    const int tok = tb + l32;
+    const bool valid = tok < S;
+    v4i x[KS];
 #pragma unroll
-    for (int i = 0; i < DW; ++i) dot = __builtin_amdgcn_sdot4(x[i], scent[jj * DW + i], dot, false);
-    const int dist = snorm[jj] - 2 * dot;
-    if (dist < best) { best = dist; lab = jj; }
-  }
-  if (valid) {
-    labels[bh * S + tok] = lab;
-    atomicAdd(&scnt[lab], 1);
-  }
-
-  for (int s0 = 0; s0 < k; s0 += SLICE) {
-    const int ns = min(SLICE, k - s0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < ns * D; i += 256) ssum[i] = 0;
-    __syncthreads();
-    if (valid && lab >= s0 && lab < s0 + ns) {
-      int32_t* row = ssum + (lab - s0) * D;
+    for (int s = 0; s < KS; ++s)
+      x[s] = valid ? *reinterpret_cast<const v4i*>(codes + (bh * S + tok) * D + 32 * s + 16 * hh)
+                   : v4i{0, 0, 0, 0};
+    int best = 0x7FFFFFFF, bidx = 0;
+    for (int ct = 0; ct < ntile; ++ct) {
+      v16i dot = {};
 #pragma unroll
-      for (int i = 0; i < DW; ++i) {
-        atomicAdd(&row[4 * i + 0], static_cast<int32_t>(static_cast<int8_t>(x[i] & 0xFF)));
-        atomicAdd(&row[4 * i + 1], static_cast<int32_t>(static_cast<int8_t>((x[i] >> 8) & 0xFF)));
-        atomicAdd(&row[4 * i + 2], static_cast<int32_t>(static_cast<int8_t>((x[i] >> 16) & 0xFF)));
-        atomicAdd(&row[4 * i + 3], static_cast<int32_t>(static_cast<int8_t>((x[i] >> 24) & 0xFF)));
+      for (int s = 0; s < KS; ++s) {
+        const v4i a = *reinterpret_cast<const v4i*>(scent + (ct * 32 + l32) * D + 32 * s + 16 * hh);
+        dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x[s], dot, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ct * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (row < k) {
+          const int dist = snorm[row] - 2 * dot[r];
+          if (dist < best) { best = dist; bidx = row; }
+        }
       }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < ns * D; i += 256)
-      if (ssum[i] != 0) atomicAdd(&sums[bh * k * D + static_cast<size_t>(s0) * D + i], ssum[i]);
+    // the other 16 centroids of each token sit in lane ^ 32
+    const auto pd = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(best),
+                                                     static_cast<unsigned>(best), false, false);
+    const auto pi = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(bidx),
+                                                     static_cast<unsigned>(bidx), false, false);
+    const int obest = static_cast<int>(hh ? pd[0] : pd[1]);
+    const int oidx = static_cast<int>(hh ? pi[0] : pi[1]);
+    if (obest < best || (obest == best && oidx < bidx)) { best = obest; bidx = oidx; }
+    if (hh == 0) {
+      slab[blk * 32 + l32] = valid ? static_cast<uint8_t>(bidx) : 0;
+      if (valid) {
+        labels[bh * S + tok] = bidx;
+        atomicAdd(&scnt[bidx], 1);
+      }
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < k; i += 256)
-    if (scnt[i] != 0) atomicAdd(&cnt[bh * k + i], scnt[i]);
+  for (int jj = threadIdx.x; jj < k; jj += 256)
+    pcnt[(bh * nasg + chunk) * k + jj] = scnt[jj];
+
+  // ---- member sums, one 32-centroid tile at a time ----
+  for (int ct = 0; ct < ntile; ++ct) {
+    v16i acc[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc[s] = v16i{};
+    const uint32_t cid = static_cast<uint32_t>(ct * 32 + l32) * 0x01010101u;
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave * BPW + i;
+      const int tb = chunk * kAsg + blk * 32;
+      if (tb >= S) break;
+      const uint4 lb = *reinterpret_cast<const uint4*>(slab + blk * 32 + 16 * hh);
+      const v4i oh = {static_cast<int>(zero_bytes_to_ones(lb.x ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.y ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.z ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.w ^ cid))};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4i xt = *reinterpret_cast<const v4i*>(codes_t + (bh * D + 32 * s + l32) * S32 + tb + 16 * hh);
+        acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oh, xt, acc[s], 0, 0, 0);
+      }
+    }
+    // lane holds channel 32 s + l32 of centroids 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        atomicAdd(&sred[(8 * (r >> 2) + 4 * hh + (r & 3)) * D + 32 * s + l32], acc[s][r]);
+    __syncthreads();
+    const int rows = min(32, k - ct * 32);
+    int32_t* dst = psum + ((bh * nasg + chunk) * k + ct * 32) * D;
+    for (int i = threadIdx.x; i < rows * D; i += 256) {
+      dst[i] = sred[i];
+      sred[i] = 0;
+    }
+    for (int i = rows * D + threadIdx.x; i < 32 * D; i += 256) sred[i] = 0;
+    __syncthreads();
+  }
 }
 
+// One thread per (centroid, channel): partials summed in chunk order.
 template <int D>
-__global__ __launch_bounds__(256) void km_update_kernel(int H, int k, int8_t* __restrict__ cent,
-                                                        int32_t* __restrict__ sums,
-                                                        int32_t* __restrict__ cnt) {
-  const int h = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(256) void km_update_kernel(int H, int k, int nasg,
+                                                        int8_t* __restrict__ cent,
+                                                        const int32_t* __restrict__ psum,
+                                                        const int32_t* __restrict__ pcnt) {
+  const int h = blockIdx.y, b = blockIdx.z;
   const size_t bh = static_cast<size_t>(b) * H + h;
-  for (int idx = threadIdx.x; idx < k * D; idx += blockDim.x) {
-    const int n = cnt[bh * k + idx / D];
-    const int s = sums[bh * k * D + idx];
-    if (n > 0) {
-      const long long mag = (2LL * (s < 0 ? -static_cast<long long>(s) : s) + n) / (2LL * n);
-      cent[bh * k * D + idx] = static_cast<int8_t>(s < 0 ? -mag : mag);
-    }
-    sums[bh * k * D + idx] = 0;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k * D) return;
+  const int jj = idx / D;
+  int n = 0;
+  long long sum = 0;
+  for (int c = 0; c < nasg; ++c) {
+    n += pcnt[(bh * nasg + c) * k + jj];
+    sum += psum[(bh * nasg + c) * k * D + idx];
   }
-  __syncthreads();
-  for (int jj = threadIdx.x; jj < k; jj += blockDim.x) cnt[bh * k + jj] = 0;
+  if (n > 0) {
+    const long long mag = (2LL * (sum < 0 ? -sum : sum) + n) / (2LL * n);
+    cent[bh * k * D + idx] = static_cast<int8_t>(sum < 0 ? -mag : mag);
+  }
 }
 
 __global__ __launch_bounds__(256) void km_hist_kernel(const int32_t* __restrict__ labels, int S,
@@ -365,14 +461,15 @@ void run_kmeans(const uint16_t* k, const uint16_t* v, int B, int S, int H, int k
   hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((bh + 255) / 256, 1024))),
                      dim3(256), 0, st, ws.amax, bh, 0u);
   hipLaunchKernelGGL(km_amax_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax);
-  hipLaunchKernelGGL(km_codes_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax, ws.codes);
-  hipLaunchKernelGGL(km_init_kernel<D>, dim3(H, B), dim3(256), 0, st, ws.codes, S, H, kc, ws.cent,
-                     ws.sums, ws.cnt);
+  hipLaunchKernelGGL(km_codes_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax, ws.codes,
+                     ws.codes_t);
+  hipLaunchKernelGGL(km_init_kernel<D>, dim3(H, B), dim3(256), 0, st, ws.codes, S, H, kc, ws.cent);
+  const int nasg = (S + kAsg - 1) / kAsg;
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(km_assign_kernel<D>, dim3(nchunk, H, B), dim3(256), 0, st, ws.codes, S, H, kc,
-                       ws.cent, labels, ws.sums, ws.cnt);
-    hipLaunchKernelGGL(km_update_kernel<D>, dim3(H, B), dim3(256), 0, st, H, kc, ws.cent, ws.sums,
-                       ws.cnt);
+    hipLaunchKernelGGL(km_assign_kernel<D>, dim3(nasg, H, B), dim3(256), 0, st, ws.codes,
+                       ws.codes_t, S, H, kc, ws.cent, labels, ws.psum, ws.pcnt);
+    hipLaunchKernelGGL(km_update_kernel<D>, dim3((kc * D + 255) / 256, H, B), dim3(256), 0, st, H,
+                       kc, nasg, ws.cent, ws.psum, ws.pcnt);
   }
   hipLaunchKernelGGL(km_hist_kernel, dim3(nchunk, H, B), dim3(256), 0, st, labels, S, H, kc, nchunk,
                      ws.chunk);
