@@ -13,7 +13,7 @@ order that VC-Attention builds on (summary, "Methodology in Plain English"
 and abstract: an online softmax that keeps a running row max and row sum):
 per tile j, with scores s in log2 units,
 
-    m'   = max(m, max_t s_t)                 running max, once per tile
+    m'   = max(m, ceil(max_t s_t))           running max, once per tile
     p_t  = 2^(s_t - m')                      FP32 exponential
     P~   = cast of p to E4M3 (see below)
     l_j  = tile row sum                      the row sum the recurrence keeps
@@ -25,6 +25,13 @@ and O = acc / l, lse2 = m + log2 l + qmu.  The last term of ``acc`` is the
 rank-one restore of the block's V mean from the tile row sum (VC-Attention
 summary, Key Contribution 1: "restored inside the existing online-softmax
 recurrence using the row sum the kernel already accumulates").
+
+Reading (integer running max): any m' no smaller than the row's scores gives
+the same softmax; the recurrence rounds the running max up to an integer, so
+2^(m - m') and the shift 2^(8 - m') of P below are exact powers of two (an
+exponent change for the matrix core's E8M0 operand scales and for the scaled
+FP8 conversion), and the max moves less often.  p_t stays in (2^-1, 1] at the
+row's largest score of the tile where the max is set.
 
 Probability casts (``pcast``):
 
@@ -58,20 +65,18 @@ that computes in FP32 takes the same decisions.  With scores S (the dot
 product of the E4M3 codes; exactly, rounded to float32, or, with
 ``qk_codes``, in the FP8 matrix core's arithmetic, ``matrix_core``):
 
-    c_j  = f32(f32(s_Q s_K,j) * c)            c = f32(softmax_scale log2 e)
-    s_t  = f32(S_t c_j)                       (only the max uses these)
-    m'   = max(m, max_t s_t)
-    e4m3:    x_t = f32(S_t c_j + f32(8 - m'))      one FMA
-             p8_t = f32(2^x_t),  P~ code = E4M3(p8_t)
-    expcast: t_t = f32(S_t f32(8 c_j) + f32(K0 - 8 m'))
+    c_j  = f32(f32(s_Q s_K,j) * c)   (the pipeline folds c into Q and passes
+                                       c = 1: c_j is then the exact product of
+                                       two power-of-two block scales)
+    s_t  = f32(S_t c_j)
+    m'   = max(m, ceil(max_t s_t))
+    e4m3:    p8_t = f32(2^(s_t + 8 - m')),  P~ code = E4M3(p8_t)
+             (2^(8 - m') is a power of two: the same value as
+             f32(2^s_t) 2^(8 - m'), which is how the kernel forms it)
+    expcast: t_t = f32(8 s_t + f32(K0 - 8 m'))
     row sum: sum of P~ (with ``qk_codes``, in the matrix core's arithmetic:
     the tile's P codes in the PV k order against an all-ones operand)
     accumulation of l and acc: float64.
-
-A one-FMA expression is evaluated in float64 (the product of two float32
-values is exact there) and rounded once to float32; that equals the
-single-rounded FMA except when the float64 sum lands on a float32 midpoint
-(probability about 2^-29 per element).
 
 With ``fp32=False`` everything is float64 and exp2 is exact to float64.
 
@@ -172,16 +177,15 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
             S_raw = rnd(q_hat @ kb[:n].T)                   # [R, n]
         cj = rnd(rnd(q_scale * float(k_scale[j])) * c)      # [R]
         s = rnd(S_raw * cj[:, None])
-        m_new = np.maximum(m, s.max(axis=1))
+        m_new = np.maximum(m, np.ceil(s.max(axis=1)))
         if pcast == "expcast":
             k0 = float(K0_F32) if fp32 else K0
             bias = rnd(k0 - 8.0 * m_new)
-            t = rnd(S_raw * rnd(8.0 * cj)[:, None] + bias[:, None])
+            t = rnd(8.0 * s + bias[:, None])
             codes = expcast_codes(t)
             p_tilde = e4m3.decode(codes) * 2.0 ** -8
         else:
-            x8 = rnd(S_raw * cj[:, None] + rnd(8.0 - m_new)[:, None])
-            p8 = rnd(np.exp2(x8))
+            p8 = rnd(np.exp2(s + (8.0 - m_new)[:, None]))
             if pcast == "e4m3":
                 codes = e4m3.encode(p8)
                 p_tilde = e4m3.decode(codes) * 2.0 ** -8

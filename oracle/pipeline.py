@@ -6,8 +6,8 @@ Test infrastructure (see ``oracle/__init__``).
    K and V permuted together (``kmeans``);
 2. exact statistics: mu_K over the sequence, mu_V per 128-token block (or
    over the sequence) (``smoothing``);
-3. per-block E4M3 quantization of Q, of K - mu_K and of the V residual
-   (power-of-two scale), and qmu = c q.mu_K from the bf16 q (``smoothing``);
+3. per-block E4M3 quantization (power-of-two scales) of c Q, of K - mu_K
+   and of the V residual, and qmu = c q.mu_K from the bf16 q (``smoothing``);
 4. the tiled recurrence with the rank-one mean restore and the chosen P cast
    (``attention``).
 
@@ -83,9 +83,9 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     out.update(k_mean=k_mean, v_mean=v_mean, vmean_mode=vmean_mode,
                v_block_means=smoothing.v_block_means(vp) if smooth else None)
 
-    q_codes, q_scale = smoothing.quantize_blocks(q)
+    q_codes, q_scale = smoothing.quantize_blocks(smoothing.prescale_queries(q, c))
     k_codes, k_scale = smoothing.quantize_blocks(kc)
-    v_codes, v_scale = smoothing.quantize_blocks(vr, pow2=True)
+    v_codes, v_scale = smoothing.quantize_blocks(vr)
     out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
                k_scale=k_scale, v_codes=v_codes, v_scale=v_scale, q_off=q_off)
 
@@ -93,7 +93,7 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
         pcast = "expcast" if expcast else "e4m3"
     o, lse2 = attention.tiled_attention(
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
-        e4m3.decode(k_codes), k_scale, e4m3.decode(v_codes), v_scale, S, c,
+        e4m3.decode(k_codes), k_scale, e4m3.decode(v_codes), v_scale, S, 1.0,
         v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
         fp32=fp32, qk_codes=(q_codes[rows], k_codes) if scores == "mfma" else None)
     out["O"], out["lse2"] = o, lse2

@@ -20,27 +20,31 @@ Sources
   "centralize V, restore its sequence mean after attention".
 * Block quantization scale: one scale per block set by the block's largest
   entry (VC-Attention abstract: "a block's quantization scale is set by its
-  largest entries").  Reading for Q and K: scale = amax / 448 over the
-  block's valid tokens and all channels, in FP32; codes = E4M3(x * (448 /
-  amax)) in FP32.  A block with amax == 0 uses scale 1 (all codes 0).
-  448 / amax is clamped to the largest finite float32 so a denormal amax
-  cannot make it infinite.  Reading for the V residual: the scale is the
-  power of two 2^e with e the smallest integer such that amax <= 448 * 2^e
-  (e >= -126; e = 0 when amax == 0), codes = E4M3(x * 2^-e).  A power-of-two
-  block scale (the E8M0 block scale of MX formats) is applied by the FP8
-  matrix core itself during PV, exactly; it leaves every value's relative
-  precision unchanged and only lets the block maximum land in (224, 448].
+  largest entries").  Reading, for Q, centred K and the V residual alike:
+  the scale is the power of two 2^e with e the smallest integer such that
+  amax <= 448 * 2^e over the block's valid tokens and all channels (e >=
+  -126; e = 0 when amax == 0), and codes = E4M3(x * 2^-e), round to nearest
+  even.  A power-of-two block scale (the E8M0 block scale of MX formats) is
+  applied by the FP8 matrix core itself, exactly, in both products; it leaves
+  every value's relative precision unchanged (E4M3 is a floating-point
+  format) and only lets the block maximum land in (224, 448] instead of at
+  448.
+* Score constant folded into Q: the scores are kept in log2 units (the
+  exponential is exp2), so Q is multiplied by c = softmax_scale * log2(e) in
+  FP32 before its quantization, as SageAttention-style FP8 attention does
+  with its softmax scale.  Reading: the pages leave open where the scale is
+  applied; with power-of-two Q and K block scales this makes the matrix
+  core's output the log2-domain score itself.
 
-Pinned by tests/test_oracle_quant.py (amax element -> +-448, reconstruction
-error within half an E4M3 step, padding, exact centring, mean error of the
-dequantized V).
+Pinned by tests/test_oracle_quant.py (the smallest fitting power of two,
+the block maximum in (224, 448], reconstruction error within half an E4M3
+step, padding, exact centring, mean error of the dequantized V).
 """
 import numpy as np
 
 from . import e4m3
 
 BLOCK = 128
-_F32_MAX = np.float32(np.finfo(np.float32).max)
 LOG2E_F32 = np.float32(1.4426950408889634)
 
 
@@ -106,12 +110,12 @@ def pow2_exponent(amax) -> int:
     return max(e, -126)
 
 
-def quantize_blocks(x, block: int = BLOCK, pow2: bool = False):
-    """Per-block E4M3 quantization of a float32 [S, D] array.
+def quantize_blocks(x, block: int = BLOCK):
+    """Per-block E4M3 quantization of a float32 [S, D] array with the
+    power-of-two block scale (reading above).
 
     Returns (codes uint8 [nb*block, D], scale float32 [nb]).  Rows past S are
     padding and get code 0.  Dequantized value = decode(code) * scale.
-    pow2: power-of-two scale (the V residual reading above).
     """
     x = np.asarray(x, dtype=np.float32)
     S, D = x.shape
@@ -120,23 +124,15 @@ def quantize_blocks(x, block: int = BLOCK, pow2: bool = False):
     scale = np.empty(nb, dtype=np.float32)
     for j in range(nb):
         xb = x[j * block:min(S, (j + 1) * block)]
-        amax = np.float32(np.max(np.abs(xb)))
-        if pow2:
-            e = pow2_exponent(amax)
-            scale[j] = np.float32(2.0 ** e)
-            codes[j * block:j * block + xb.shape[0]] = e4m3.encode(xb.astype(np.float64) * 2.0 ** -e)
-            continue
-        if amax > 0:
-            s = np.float32(amax / np.float32(448.0))
-            inv = np.float32(np.float32(448.0) / amax)
-            if not np.isfinite(inv):
-                inv = _F32_MAX
-        else:
-            s = np.float32(1.0)
-            inv = np.float32(1.0)
-        scale[j] = s
-        codes[j * block:j * block + xb.shape[0]] = e4m3.encode((xb * inv).astype(np.float32))
+        e = pow2_exponent(np.float32(np.max(np.abs(xb))))
+        scale[j] = np.float32(2.0 ** e)
+        codes[j * block:j * block + xb.shape[0]] = e4m3.encode(xb.astype(np.float64) * 2.0 ** -e)
     return codes, scale
+
+
+def prescale_queries(q, c) -> np.ndarray:
+    """float32 q * c (one float32 rounding): Q in log2-score units."""
+    return (np.asarray(q, dtype=np.float32) * np.float32(c)).astype(np.float32)
 
 
 def dequantize_blocks(codes, scale, S: int, block: int = BLOCK) -> np.ndarray:

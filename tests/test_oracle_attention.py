@@ -115,14 +115,16 @@ def test_joint_permutation_invariance():
 
 
 def _quantized_case(rng, S, D, q, k, v, smooth=True):
+    """Quantized operands as the pipeline forms them: c folded into Q, so the
+    score constant handed to the recurrence is 1."""
     c = smoothing.score_constant(np.float32(1.0 / math.sqrt(D)))
     kc = smoothing.centre(k, smoothing.k_seq_mean(k)) if smooth else k
     bm = smoothing.v_block_means(v)
     r = smoothing.residual_blocks(v, bm) if smooth else v
-    qc, qs = smoothing.quantize_blocks(q)
+    qc, qs = smoothing.quantize_blocks(smoothing.prescale_queries(q, c))
     kcodes, ks = smoothing.quantize_blocks(kc)
     vcodes, vs = smoothing.quantize_blocks(r)
-    return c, qc, qs, kcodes, ks, vcodes, vs, bm
+    return 1.0, qc, qs, kcodes, ks, vcodes, vs, bm
 
 
 def test_constant_v_is_returned_exactly_with_block_mean_restore():
@@ -141,8 +143,10 @@ def test_constant_v_is_returned_exactly_with_block_mean_restore():
 
 
 def test_equal_scores_give_the_mean_of_dequantized_v():
-    """All keys identical: every p is 1, code 0x78 exactly, so O is the plain
-    average of the dequantized V rows and lse2 = s_max + log2 S + qmu."""
+    """All keys identical: every p of a row is the same power 2^(s - m'), so
+    every code of the row is the same and O is the plain average of the
+    dequantized V rows; lse2 = m' + log2(S P~) with P~ = E4M3(2^(s+8-m'))/2^8,
+    within half an E4M3 step of s + log2 S."""
     rng = np.random.default_rng(5)
     S, D = 300, 64
     q = rng.standard_normal((S, D)).astype(np.float32)
@@ -152,21 +156,27 @@ def test_equal_scores_give_the_mean_of_dequantized_v():
     rows = np.arange(0, S, 13)
     o, lse2, tr = attention.tiled_attention(e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes), ks,
                                             e4m3.decode(vcodes), vs, S, c, return_trace=True)
+    srow = np.array([float(np.float32(np.float32(e4m3.decode(qc[i]) @ e4m3.decode(kcodes[0])) *
+                                      np.float32(np.float32(qs[i // 128] * ks[0]) * c))) for i in rows])
+    mrow = np.ceil(srow)
+    code = e4m3.encode(np.exp2(srow + 8.0 - mrow).astype(np.float32))
     for codes in tr["codes"]:
-        assert np.all(codes == 0x78)
+        assert np.all(codes == code[:, None])
     deq = smoothing.dequantize_blocks(vcodes, vs, S)
-    # every P~ is exactly 1, and l sums the P~
+    # the P~ of a row are all equal, and l sums the P~
     np.testing.assert_allclose(o, np.repeat(deq.mean(0)[None], len(rows), 0), rtol=1e-14, atol=0)
-    srow = [float(np.float32(np.float32(e4m3.decode(qc[i]) @ e4m3.decode(kcodes[0])) *
-                             np.float32(np.float32(qs[i // 128] * ks[0]) * c))) for i in rows]
-    np.testing.assert_allclose(lse2, np.array(srow) + math.log2(S), rtol=0, atol=1e-5)
+    expect = mrow + np.log2(S * e4m3.decode(code) / 256.0)
+    np.testing.assert_allclose(lse2, expect, rtol=0, atol=1e-12)
+    assert np.all(np.abs(lse2 - (srow + math.log2(S))) <= math.log2(1 + 2.0 ** -4) + 1e-12)
 
 
 def test_e4m3_p_cast_error_is_within_half_a_step():
     """With exact operands, the E4M3 P cast (2^8 scale) changes each p by at
     most 2^-4 of itself (p >= 2^-14), so the normalized weights P~/sum(P~)
-    are within total variation 2^-4 (plus the mass below the normal range)
-    of p/sum(p), and each output channel within that share of its range."""
+    are within total variation 2^-4 (plus the mass below the normal range,
+    at most 2^-18 per key against a row sum of at least 1/2, the row max
+    having p in (1/2, 1]) of p/sum(p), and each output channel within that
+    share of its range."""
     rng = np.random.default_rng(6)
     S, D = 700, 64
     q = rng.standard_normal((20, D)) * 2
@@ -182,7 +192,7 @@ def test_e4m3_p_cast_error_is_within_half_a_step():
                                       pcast="e4m3", fp32=False)
     err = np.abs(oc - od)
     diam = v.max(axis=0) - v.min(axis=0)
-    assert np.all(err <= (2.0 ** -4 + S * 2.0 ** -18) * diam[None, :])
+    assert np.all(err <= (2.0 ** -4 + S * 2.0 ** -17) * diam[None, :])
     assert np.all(err.max(axis=1) > 0)          # the cast really happened
 
 
@@ -231,8 +241,9 @@ def test_expcast_tv_bound_on_random_rows():
         assert tv <= attention.EXPCAST_TV_BOUND + tail + 1e-12
         worst = max(worst, tv - tail)
         # per element: log2 error within sigma + 1/16 where the code is normal
+        # (codes are relative to the integer running max)
         nz = codes != 0
-        err = np.log2(e4m3.decode(codes[nz]) / 256.0) - (s[nz] - s.max())
+        err = np.log2(e4m3.decode(codes[nz]) / 256.0) - (s[nz] - np.ceil(s.max()))
         assert np.all(np.abs(err) <= attention.EXPCAST_LOG2_ERR + 1e-12)
     assert worst > 0.005
 
@@ -284,3 +295,34 @@ def test_expcast_output_bound_by_value_diameter():
         tail = p[codes == 0].sum()
         diam = v.max(0) - v.min(0)
         assert np.all(np.abs(ph @ v - p @ v) <= (attention.EXPCAST_TV_BOUND + tail) * diam + 1e-12)
+
+
+def test_score_constant_folded_into_q_gives_log2_scores():
+    """Q quantized as c Q (c = softmax_scale log2 e) and the recurrence run
+    with c = 1 is softmax attention of the dequantized operands in log2 units:
+    exactly dense attention of (deq Q, deq K) at scale ln 2 when P is not
+    cast; applying c a second time (or not at all) is far off."""
+    rng = np.random.default_rng(8)
+    S, D = 300, 64
+    q = rng.standard_normal((S, D)).astype(np.float32) * 2
+    k = rng.standard_normal((S, D)).astype(np.float32)
+    v = rng.standard_normal((S, D)).astype(np.float32)
+    c1, qc, qs, kcodes, ks, vcodes, vs, _ = _quantized_case(rng, S, D, q, k, v, smooth=False)
+    assert c1 == 1.0
+    rows = np.arange(0, S, 11)
+    qd = e4m3.decode(qc[rows]) * qs[rows // 128, None].astype(np.float64)
+    kd = smoothing.dequantize_blocks(kcodes, ks, S)
+    vd = smoothing.dequantize_blocks(vcodes, vs, S)
+    od, ld = attention.dense_attention(qd, kd, vd, math.log(2.0))
+    ot, lt = attention.tiled_attention(e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes),
+                                       ks, e4m3.decode(vcodes), vs, S, 1.0, pcast="none", fp32=False)
+    np.testing.assert_allclose(ot, od, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lt, ld, rtol=0, atol=1e-12)
+    # and it approximates attention of the original operands at 1/sqrt(D)
+    o0, _ = attention.dense_attention(q[rows], k, v, 1.0 / math.sqrt(D))
+    rel = lambda o: np.linalg.norm(o - o0) / np.linalg.norm(o0)  # noqa: E731
+    assert rel(ot) < 0.1
+    c = float(smoothing.score_constant(np.float32(1.0 / math.sqrt(D))))
+    o2, _ = attention.tiled_attention(e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes),
+                                      ks, e4m3.decode(vcodes), vs, S, c, pcast="none", fp32=False)
+    assert rel(o2) > 10 * rel(ot)

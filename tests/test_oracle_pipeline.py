@@ -62,7 +62,10 @@ def test_expcast_pipeline_error_is_bounded():
     r0 = pipeline.smoothed_attention_head(q, k, v, rows=rows, expcast=False)
     e1 = pipeline.error_report(r1["O"], ref)["rel_l2"]
     e0 = pipeline.error_report(r0["O"], ref)["rel_l2"]
-    assert e0 < e1 < 0.2
+    # ExpCast adds at most its weight error (Proposition 3.1, total
+    # variation <= 3.64% plus the underflow tail) on top of the E4M3 cast;
+    # on one small head either may come out ahead
+    assert e0 < 0.2 and e1 < e0 + 2 * attention.EXPCAST_TV_BOUND
 
 
 def test_sample_rows_cover_edges():

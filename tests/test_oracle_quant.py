@@ -33,32 +33,13 @@ def test_block_means_cover_ragged_last_block():
     np.testing.assert_array_equal(bm[0], smoothing.exact_mean_f32(v[:128]))
 
 
-def test_amax_element_encodes_to_448_and_error_bound():
-    rng = np.random.default_rng(2)
-    x = (rng.standard_normal((300, 64)) * rng.uniform(0.01, 50, (300, 1))).astype(np.float32)
-    codes, scale = smoothing.quantize_blocks(x)
-    assert codes.shape == (384, 64) and scale.shape == (3,)
-    for j in range(3):
-        xb = x[j * 128:min(300, (j + 1) * 128)]
-        cb = codes[j * 128:j * 128 + xb.shape[0]]
-        i = np.unravel_index(np.argmax(np.abs(xb)), xb.shape)
-        assert cb[i] in (0x7E, 0xFE)
-        assert scale[j] == np.float32(np.abs(xb).max() / np.float32(448))
-        rec = e4m3.decode(cb) * float(scale[j])
-        inv = np.float32(448) / np.float32(np.abs(xb).max())
-        y = (xb * inv).astype(np.float32).astype(np.float64)
-        bound = (e4m3.ulp_half(np.abs(y)) + np.abs(y) * 2.0 ** -23) * float(scale[j])
-        assert np.all(np.abs(rec - xb) <= bound * 1.0001)
-    # padding rows of the ragged last block are code 0
-    assert np.all(codes[300:] == 0)
-
-
 def test_zero_block_uses_unit_scale():
     x = np.zeros((130, 16), dtype=np.float32)
     x[128:] = 1.0
     codes, scale = smoothing.quantize_blocks(x)
     assert scale[0] == 1.0 and np.all(codes[:128] == 0)
-    assert np.all(codes[128:130] == 0x7E)
+    # amax 1 -> scale 2^-8 (1 <= 448/256 and 1 > 448/512): code of 256
+    assert scale[1] == 2.0 ** -8 and np.all(codes[128:130] == 0x78)
 
 
 def test_centring_removes_the_sequence_mean():
@@ -118,19 +99,23 @@ def test_q_log2_offset_is_the_row_shift_of_centring():
 
 
 def test_pow2_scale_is_the_smallest_fitting_power_of_two():
+    """Block scale 2^e: the smallest power of two with amax <= 448 2^e, the
+    block maximum's code in (224, 448], every value within half an E4M3 step,
+    padding rows code 0."""
     rng = np.random.default_rng(6)
     for amax in [1e-30, 0.3, 1.0, 447.0, 448.0, 448.5, 896.0, 897.0, 3e5]:
         e = smoothing.pow2_exponent(np.float32(amax))
         assert amax <= 448 * 2.0 ** e and (e == -126 or amax > 448 * 2.0 ** (e - 1))
     assert smoothing.pow2_exponent(0.0) == 0
     x = (rng.standard_normal((300, 32)) * rng.uniform(0.01, 50, (300, 1))).astype(np.float32)
-    codes, scale = smoothing.quantize_blocks(x, pow2=True)
+    codes, scale = smoothing.quantize_blocks(x)
     for j in range(3):
         xb = x[j * 128:min(300, (j + 1) * 128)]
         e = np.log2(float(scale[j]))
         assert e == np.round(e)                                    # a power of two
         m = np.abs(e4m3.decode(codes[j * 128:j * 128 + len(xb)])).max()
         assert 224 < m <= 448                                      # the max lands in (224, 448]
+        assert scale[j] == np.float32(2.0 ** smoothing.pow2_exponent(np.abs(xb).max()))
         rec = e4m3.decode(codes[j * 128:j * 128 + len(xb)]) * float(scale[j])
         y = np.abs(xb.astype(np.float64)) / float(scale[j])
         assert np.all(np.abs(rec - xb) <= e4m3.ulp_half(y) * float(scale[j]) * 1.0000001)
