@@ -74,13 +74,12 @@ def vs_quantize_residual(q, k, v, kv_layout, shape, softmax_scale, k_mean, v_mea
 
 
 def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, shape,
-                    softmax_scale, flags, out, lse2):
+                    flags, out, lse2):
     B, S, H, D = shape
     dev = _dev(q8, k8, v8)
     check(load().vs_fp8_attn_fwd(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v8), _p(v_scale),
-                                 _p(v_mean), vmean_mode, _p(q_mu), B, S, H, D,
-                                 float(softmax_scale), int(flags), _p(out), _p(lse2),
-                                 _stream(dev)), "vs_fp8_attn_fwd")
+                                 _p(v_mean), vmean_mode, _p(q_mu), B, S, H, D, int(flags),
+                                 _p(out), _p(lse2), _stream(dev)), "vs_fp8_attn_fwd")
 
 
 def vs_kmeans_workspace_bytes(B, S, H, D, k_clusters):
@@ -167,8 +166,8 @@ class Plan:
     def attn(self):
         """The attention call alone, on the buffers the last ``run`` filled."""
         vs_fp8_attn_fwd(self.q8, self.q_scale, self.k8, self.k_scale, self.v8, self.v_scale,
-                        self.v_mean, self.vmean_mode, self.q_mu, self.shape, self.softmax_scale,
-                        self.flags, self.out, self.lse2)
+                        self.v_mean, self.vmean_mode, self.q_mu, self.shape, self.flags,
+                        self.out, self.lse2)
 
 
 def attention(q, k, v, **kw):

@@ -17,17 +17,21 @@
 //   groups run a ping-pong one phase apart, separated by workgroup barriers:
 //   while one wave issues its matrix-core phase, the other wave on the SIMD
 //   runs its vector phase.
-//     M(j): S^T = K_j Q^T on v_mfma_f32_32x32x64_f8f6f4 (A = 32 keys x 64
-//       channels from LDS, B = the wave's 32 queries, held in registers for
-//       the whole loop; a lane owns one query (lane % 32) and 16 keys per
-//       32-key sub-tile), then for tile j - 1: the row sum of its E4M3
+//     M(j): S^T = K_j Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (A = 32 keys x
+//       64 channels from LDS, B = the wave's 32 queries, held in registers
+//       for the whole loop; a lane owns one query (lane % 32) and 16 keys per
+//       32-key sub-tile; the power-of-two K and Q block scales are the E8M0
+//       operand scales, and Q carries softmax_scale * log2 e, so the product
+//       is the score in log2 units), then for tile j - 1: the row sum of its E4M3
 //       probabilities (P codes against an all-ones A operand), O^T +=
 //       2^e 2^-8 V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (the
 //       power-of-two V block scale and P's 2^8 are E8M0 operand scales, so
 //       the product accumulates straight into acc), and the rank-one restore
 //       acc += mu (x) l as v_mfma_f32_32x32x1_2b_f32 outer products.
-//     V(j): tile max (one cross-half exchange), running max, O^T rescale
-//       (only when some row's max moved), and P packed to E4M3 straight into
+//     V(j): tile max (one cross-half exchange), integer running max, O^T
+//       rescale by an exact power of two (only when some row's max moved),
+//       and P = E4M3(2^s / 2^(m - 8)) -- exp2 of the score and the scaled
+//       FP8 pack, whose power-of-two scale applies the offset -- packed straight into
 //       the B operand of PV: the accumulator layout of two key sub-tiles is
 //       exactly one 64-token k-step of the PV MFMA, given that V is stored in
 //       the matching token order (vs_quantize_residual).
@@ -50,6 +54,8 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr float kExpcastK0 = 119.66015f;   // 120 - 4 (log2(1.5) - 1/2)
 
+typedef short v2s __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   v8i r;
   r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
@@ -60,6 +66,9 @@ __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+
+// E8M0 byte of a power-of-two float scale (its biased exponent).
+__device__ __forceinline__ int e8m0_of(float pow2) { return (__float_as_int(pow2) >> 23) & 0xFF; }
 
 // Same product with E8M0 operand scales (byte b means 2^(b - 127)).
 __device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, const v16f& c,
@@ -113,7 +122,7 @@ struct Ctx {
   rsrc_t krs, vrs, murs;                 // this head's K codes, V codes, V block means
   const float* ksc;                      // K block scales of this head
   const float* vsc;                      // V block scales of this head
-  float sq, c_log2;
+  int q_e8;                              // E8M0 byte of this query block's scale
   int nb, S, dma_wave, hh, lane;         // dma_wave: 0-3 in the DMA group, else -1
   int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
   int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
@@ -121,10 +130,10 @@ struct Ctx {
   v8i ones;                              // E4M3 ones, A operand of the row sums
 };
 
-// Recurrence state of one wave: raw scores s of the current key tile, its
-// E4M3 probabilities pb, the running max m, the factor alpha of the last
-// tile (applied to O^T already, to l when that tile's row sum is known), O^T
-// and l.
+// Recurrence state of one wave: log2-domain scores s of the current key
+// tile, its E4M3 probabilities pb, the integer running max m, the factor
+// alpha of the last tile (applied to O^T already, to l when that tile's row
+// sum is known), O^T and l.
 template <int D>
 struct State {
   v16f s[4];
@@ -132,7 +141,7 @@ struct State {
   v16f acc[D / 32];
   float m, alpha, l;
   // block scales one tile ahead of their use (scalar loads complete while a
-  // whole phase runs): K scale of the next V phase's tile, V scale of the
+  // whole phase runs): K scale of the next M phase's QK tile, V scale of the
   // next M phase's PV tile
   float ks, vs;
 };
@@ -199,15 +208,35 @@ __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
   return max_with_other_half(mx);
 }
 
-// E4M3 probability codes of 4 scores of one lane: the dword w of sub-tile t
-// of the B operand of PV.
+// E4M3 probability codes of 4 scores of one lane (the dword w of sub-tile t
+// of the B operand of PV), |m| <= 64: 2^s is finite and normal down to where
+// its code is 0, and the pack divides it by 2^(m - 8) exactly before
+// rounding to nearest even.
+__device__ __forceinline__ int p_codes4_fast(const v16f& s, int w, float sc) {
+  const float e0 = __builtin_amdgcn_exp2f(s[4 * w + 0]);
+  const float e1 = __builtin_amdgcn_exp2f(s[4 * w + 1]);
+  const float e2 = __builtin_amdgcn_exp2f(s[4 * w + 2]);
+  const float e3 = __builtin_amdgcn_exp2f(s[4 * w + 3]);
+  // the high half is written next, so the low write may keep any upper
+  // bits: reuse e0's register instead of a zeroed one
+  v2s o;
+  __builtin_memcpy(&o, &e0, 4);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, e0, e1, sc, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, e2, e3, sc, true);
+  int pk;
+  __builtin_memcpy(&pk, &o, 4);
+  return pk;
+}
+
+// The same codes for any m (exp2 of s + 8 - m, rounded to float32 first),
+// or the ExpCast codes.
 template <bool EXPCAST, bool CAP>
-__device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bias, float c8) {
+__device__ __forceinline__ int p_codes4(const v16f& s, int w, float bias) {
   if (!EXPCAST) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 0], cj, bias));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 1], cj, bias));
-    const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 2], cj, bias));
-    const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + 3], cj, bias));
+    const float p0 = __builtin_amdgcn_exp2f(s[4 * w + 0] + bias);
+    const float p1 = __builtin_amdgcn_exp2f(s[4 * w + 1] + bias);
+    const float p2 = __builtin_amdgcn_exp2f(s[4 * w + 2] + bias);
+    const float p3 = __builtin_amdgcn_exp2f(s[4 * w + 3] + bias);
     // the high half is written next, so the low write may keep any upper
     // bits: reuse p0's register instead of a zeroed one
     uint32_t pk = cvt_pk_e4m3<false>(p0, p1, __float_as_uint(p0));
@@ -222,7 +251,7 @@ __device__ __forceinline__ int p_codes4(const v16f& s, int w, float cj, float bi
   uint32_t pk = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float x = __builtin_fmaf(s[4 * w + e], c8, bias);
+    float x = __builtin_fmaf(s[4 * w + e], 8.0f, bias);
     if (CAP) x = __builtin_fminf(x, 126.0f);
     pk = __builtin_amdgcn_cvt_pk_u8_f32(x, e, pk);
   }
@@ -239,7 +268,10 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
                                            const uint8_t* kb, const uint8_t* vb,
                                            const float* mub) {
   constexpr int KD = D / 64, DT = D / 32;
+  // the matrix-core phase issues first when both waves of the SIMD are ready
+  __builtin_amdgcn_s_setprio(1);
   if (j < c.nb) {
+    const int ks_e8 = e8m0_of(st.ks);
     // sub-tile major is fine here: the products of other waves fill the gap
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
@@ -247,7 +279,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
       for (int t = 0; t < 4; ++t) {
         const uint8_t* kr = kb + t * 32 * D;
         const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][1]));
-        st.s[t] = mfma_fp8(a, c.qa[kd], kd == 0 ? v16f{} : st.s[t]);
+        st.s[t] = mfma_fp8_scaled(a, c.qa[kd], kd == 0 ? v16f{} : st.s[t], ks_e8, c.q_e8);
       }
   }
   if (j >= 1) {
@@ -303,17 +335,17 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
     // after the last LDS read of the phase, so no wait joins the two
     st.vs = c.vsc[j < c.nb ? j : c.nb - 1];
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Vector phase V(j) of one wave, j < nb: mask (ragged last tile), tile max,
-// running max, O^T rescale, E4M3 probabilities of key tile j.
+// integer running max, O^T rescale, E4M3 probabilities of key tile j.
 template <int D, bool EXPCAST>
 __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D>& st) {
   constexpr int DT = D / 32;
   if (j == c.nb - 1 && (c.S & (kBlock - 1))) mask_tile(st.s, c.S - j * kBlock, c.hh);
-  const float cj = (c.sq * st.ks) * c.c_log2;
-  const float m_new = __builtin_fmaxf(st.m, tile_max(st.s) * cj);
-  st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(tile_max(st.s)));
+  st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // a power of two (0 on tile 0)
   if (__ballot(st.alpha != 1.0f)) {
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -321,17 +353,27 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D
       for (int r = 0; r < 16; ++r) st.acc[t][r] *= st.alpha;
   }
   st.m = m_new;
-  const float bias = EXPCAST ? kExpcastK0 - 8.0f * m_new : 8.0f - m_new;
-  // ExpCast pre-codes stay below 126.5 unless rounding of 8 m' is coarse
-  // (|m'| >= 2^20 log2 units): only then is the cap applied per element
-  if (EXPCAST && __ballot(__builtin_fabsf(m_new) >= 1048576.0f)) {
+  if (EXPCAST) {
+    const float bias = kExpcastK0 - 8.0f * m_new;
+    // ExpCast pre-codes stay below 126.5 unless rounding of 8 m is coarse
+    // (|m| >= 2^20 log2 units): only then is the cap applied per element
+    if (__ballot(__builtin_fabsf(m_new) >= 1048576.0f)) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      st.pb[q >> 3][q & 7] = p_codes4<true, true>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+      for (int q = 0; q < 16; ++q)
+        st.pb[q >> 3][q & 7] = p_codes4<true, true>(st.s[q >> 2], q & 3, bias);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        st.pb[q >> 3][q & 7] = p_codes4<true, false>(st.s[q >> 2], q & 3, bias);
+    }
+  } else if (!__ballot(__builtin_fabsf(m_new) > 64.0f)) {
+    const float sc = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_new) - 8);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) st.pb[q >> 3][q & 7] = p_codes4_fast(st.s[q >> 2], q & 3, sc);
   } else {
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      st.pb[q >> 3][q & 7] = p_codes4<EXPCAST, false>(st.s[q >> 2], q & 3, cj, bias, 8.0f * cj);
+      st.pb[q >> 3][q & 7] = p_codes4<false, false>(st.s[q >> 2], q & 3, 8.0f - m_new);
   }
   st.ks = c.ksc[j + 1 < c.nb ? j + 1 : j];
 }
@@ -366,8 +408,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, const float* __restrict__ q_mu, int S, int H,
-    int nb, int npairs, int total, float c_log2, float* __restrict__ out,
-    float* __restrict__ lse2) {
+    int nb, int npairs, int total, float* __restrict__ out, float* __restrict__ lse2) {
   constexpr int KD = D / 64;                 // k-steps of the QK product
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
   constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
@@ -411,7 +452,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   c.hh = hh;
   c.nb = nb;
   c.S = S;
-  c.c_log2 = c_log2;
   const int qrow = qb * kBlock + (wave & 3) * 32 + l32;
   {
     const uint8_t* qptr = q8 + (bh * S_pad + qrow) * D + 32 * hh;
@@ -420,7 +460,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
       c.qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qptr + 64 * kd),
                           *reinterpret_cast<const uint4*>(qptr + 64 * kd + 16));
   }
-  c.sq = q_scale[bh * nb + qb];
+  c.q_e8 = e8m0_of(q_scale[bh * nb + qb]);
   c.krs = make_rsrc(k8 + bh * S_pad * D, S_pad * D);
   c.vrs = make_rsrc(v8 + bh * S_pad * D, S_pad * D);
   c.murs = make_rsrc(VMEAN == VS_VMEAN_BLOCK ? v_mean + bh * nb * D : v_mean,
@@ -500,18 +540,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 template <int D, bool EXPCAST>
 void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
                const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
-               const float* vm, const float* qmu, int S, int H, int nb, int npairs, float c,
+               const float* vm, const float* qmu, int S, int H, int nb, int npairs,
                float* out, float* lse2) {
   const dim3 grid(total), block(512);
   if (vmean_mode == VS_VMEAN_BLOCK)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
   else if (vmean_mode == VS_VMEAN_SEQ)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, c, out, lse2);
+                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
 }
 
 }  // namespace
@@ -520,14 +560,13 @@ void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, con
 extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                                const float* k_scale, const uint8_t* v8, const float* v_scale,
                                const float* v_mean, int vmean_mode, const float* q_mu, int B,
-                               int S, int H, int D, float softmax_scale, unsigned flags,
-                               float* out, float* lse2, void* stream) {
+                               int S, int H, int D, unsigned flags, float* out, float* lse2,
+                               void* stream) {
   using namespace vs;
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
     return VS_ERR_INVALID_ARG;
   if (flags & ~VS_EXPCAST) return VS_ERR_INVALID_ARG;
-  if (!(softmax_scale > 0.0f) || !(softmax_scale <= FLT_MAX)) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
@@ -544,16 +583,15 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   // one head's codes are addressed through a 32-bit buffer range
   if (static_cast<long long>(nb) * kBlock * D > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
 
-  const float c = softmax_scale * 1.44269504088896341f;
   hipStream_t st = as_stream(stream);
   const bool ec = (flags & VS_EXPCAST) != 0;
   const int tot = static_cast<int>(total);
   if (D == 128) {
-    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
-    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
+    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
+    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
   } else {
-    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
-    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, c, out, lse2);
+    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
+    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
   }
   return launch_status();
 }

@@ -1,14 +1,14 @@
 // vs_quantize_residual: per-128-token-block E4M3 quantizers.
 //
 // TeleFuser PR #40 ("Changes"): K is centred by its sequence mean in FP32
-// before E4M3 quantization and Q is left unchanged.  VC-Attention summary
-// (Key Contribution 1): each hardware block subtracts its V mean and only the
-// residual is quantized.  The block's scale is set by its largest entry
-// (VC-Attention abstract): scale = amax / 448, codes = E4M3(x * (448/amax)).
-//
-// The V residual's scale is the power of two 2^e, e the smallest integer with
-// amax <= 448 * 2^e (e >= -126): an E8M0 block scale that the FP8 matrix core
-// applies itself during PV.
+// before E4M3 quantization.  VC-Attention summary (Key Contribution 1): each
+// hardware block subtracts its V mean and only the residual is quantized.
+// The block's scale is set by its largest entry (VC-Attention abstract): the
+// power of two 2^e, e the smallest integer with amax <= 448 * 2^e (e >= -126),
+// codes = E4M3(x * 2^-e), for Q, centred K and the V residual alike -- an
+// E8M0 block scale that the FP8 matrix core applies itself in QK^T and PV.
+// Q is multiplied by c = softmax_scale * log2(e) in FP32 first, so the QK^T
+// product is the score in log2 units.
 //
 // One workgroup per (block, head, batch).  The block (128 tokens x D) is read
 // once from HBM into registers (64 values per thread at D = 128), reduced to
@@ -75,23 +75,22 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int l
   }
 }
 
-__device__ __forceinline__ void scale_of(float amax, float& scale, float& inv) {
-  if (amax > 0.0f) {
-    scale = amax / 448.0f;
-    inv = 448.0f / amax;
-    if (!(inv <= FLT_MAX)) inv = FLT_MAX;
-  } else {
-    scale = 1.0f;
-    inv = 1.0f;
-  }
+// Smallest e >= -126 with amax <= 448 * 2^e (0 when amax == 0).
+__device__ __forceinline__ int pow2_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = ilogbf(amax) - 8;
+  while (amax > ldexpf(448.0f, e)) ++e;
+  while (e > -126 && amax <= ldexpf(448.0f, e - 1)) --e;
+  return e < -126 ? -126 : e;
 }
 
-// Q (mean == nullptr) or centred K: codes as token rows.  With q_mu != nullptr
-// also q_mu[s] = c * (q_s . k_mean) from the uncentred values.
+// Q (mean == nullptr, scaled by pre = c) or centred K (pre = 1): codes as
+// token rows.  With q_mu != nullptr also q_mu[s] = c * (q_s . k_mean) from
+// the bf16 q.
 template <int D>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
-    const float* __restrict__ mean, uint8_t* __restrict__ codes,
+    const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out, const float* __restrict__ k_mean,
     float* __restrict__ q_mu, float c_log2) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
@@ -120,15 +119,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     }
   }
 
+  if (pre != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[i][e] *= pre;
+  }
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(val[i][e]));
   const float amax = block_amax(a, red4);
-  float scale, inv;
-  scale_of(amax, scale, inv);
-  if (threadIdx.x == 0) scale_out[bh * nb + j] = scale;
+  const int ex = pow2_exponent(amax);
+  const float inv = ldexpf(1.0f, -ex);
+  if (threadIdx.x == 0) scale_out[bh * nb + j] = ldexpf(1.0f, ex);
 
   const size_t S_pad = static_cast<size_t>(nb) * kBlock;
 #pragma unroll
@@ -141,15 +146,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     w1 = cvt_pk_e4m3<true>(clamp448(val[i][6] * inv), clamp448(val[i][7] * inv), w1);
     *reinterpret_cast<uint2*>(codes + (bh * S_pad + tok) * D + 8 * c) = make_uint2(w0, w1);
   }
-}
-
-// Smallest e >= -126 with amax <= 448 * 2^e (0 when amax == 0).
-__device__ __forceinline__ int pow2_exponent(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  int e = ilogbf(amax) - 8;
-  while (amax > ldexpf(448.0f, e)) ++e;
-  while (e > -126 && amax <= ldexpf(448.0f, e - 1)) --e;
-  return e < -126 ? -126 : e;
 }
 
 // Residual V: codes transposed per block, [D][128] in the MFMA token order,
@@ -242,16 +238,16 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
   const dim3 grid(nb, H, B), block(256);
   if (D == 128) {
     hipLaunchKernelGGL(quant_rows_kernel<128>, grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
+                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
     hipLaunchKernelGGL(quant_rows_kernel<128>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       k8, k_scale, nullptr, nullptr, c_log2);
+                       1.0f, k8, k_scale, nullptr, nullptr, c_log2);
     hipLaunchKernelGGL(quant_vt_kernel<128>, grid, block, 0, st, v, kv_layout, S, H, nb, v_mean,
                        vmean_mode, v8, v_scale);
   } else {
     hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
+                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
     hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       k8, k_scale, nullptr, nullptr, c_log2);
+                       1.0f, k8, k_scale, nullptr, nullptr, c_log2);
     hipLaunchKernelGGL(quant_vt_kernel<64>, grid, block, 0, st, v, kv_layout, S, H, nb, v_mean,
                        vmean_mode, v8, v_scale);
   }

@@ -96,14 +96,15 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
 /*
  * vs_quantize_residual -- per-128-token-block E4M3 quantizers for Q, centred
  * K and residual V.  Source: TeleFuser PR #40, "Changes" (centre K in FP32
- * before E4M3; Q unchanged) and VC-Attention summary, Key Contribution 1
+ * before E4M3) and VC-Attention summary, Key Contribution 1
  * (each hardware block subtracts its mean and quantizes only the residual);
  * scale set by the block's largest entry (VC-Attention abstract).
  *
  *   q             bf16 [B,S,H,D] (always BSHD).
  *   k, v          bf16 in `kv_layout` (VS_LAYOUT_BSHD or VS_LAYOUT_BHSD).
- *   softmax_scale the attention scale (1/sqrt(D) is the usual value); used
- *                 for q_mu only.
+ *   softmax_scale the attention scale (1/sqrt(D) is the usual value): Q is
+ *                 multiplied by c = softmax_scale * log2(e) in FP32 before
+ *                 its quantization, and q_mu uses the same c.
  *   k_mean        f32 [B,H,D] from vs_smooth_stats, or NULL: no K centring.
  *   v_mean        f32 [B,H,nb,D] (VS_VMEAN_BLOCK) or [B,H,D] (VS_VMEAN_SEQ),
  *                 or NULL with VS_VMEAN_NONE.
@@ -114,17 +115,16 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
  *                   t(p) = 64*(p/64) + 32*((p%32)/16) + 8*((p%16)/4)
  *                          + 4*((p%64)/32) + p%4
  *                 (the order the attention kernel's FP8 MFMA consumes).
- *   q_scale, k_scale, v_scale  out f32 [B,H,nb]: dequantization scales
- *                 (v_scale is a power of two, see below).
- *   q_mu          out f32 [B,H,S]: c * (q . k_mean) with c = softmax_scale *
- *                 log2(e), from the bf16 q; required iff k_mean != NULL.
- * Per block: x = float32 input (minus the mean, one float32 subtraction),
- * amax = max |x| over the valid tokens and D channels, scale = amax / 448,
- * code = E4M3(x * (448 / amax)) round-to-nearest-even, saturating at 448
- * (448 / amax clamped to FLT_MAX); amax == 0 gives scale 1 and codes 0.
- * The V residual uses the power-of-two scale 2^e, e the smallest integer
- * >= -126 with amax <= 448 * 2^e, codes = E4M3(x * 2^-e): an E8M0 block scale
- * that the FP8 matrix core applies exactly during PV.
+ *   q_scale, k_scale, v_scale  out f32 [B,H,nb]: dequantization scales,
+ *                 each a power of two.
+ *   q_mu          out f32 [B,H,S]: c * (q . k_mean) from the bf16 q;
+ *                 required iff k_mean != NULL.
+ * Per block: x = float32 input (Q times c, K minus its mean, V minus its
+ * mean: one float32 operation), amax = max |x| over the valid tokens and D
+ * channels, scale = 2^e with e the smallest integer >= -126 such that
+ * amax <= 448 * 2^e (e = 0 when amax == 0), codes = E4M3(x * 2^-e), round to
+ * nearest even: an E8M0 block scale that the FP8 matrix core applies exactly
+ * in QK^T and PV.
  */
 int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, int kv_layout, int B, int S, int H,
@@ -141,7 +141,10 @@ int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
  * and PV, FP32 softmax between them); FastVideo PR #2048, "Test Results"
  * (output and log2-LSE).
  *
- *   q8, q_scale, k8, k_scale, v8, v_scale  from vs_quantize_residual.
+ *   q8, q_scale, k8, k_scale, v8, v_scale  from vs_quantize_residual (the
+ *                 power-of-two block scales; q8 encodes c * Q, so the
+ *                 product of the codes and scales is the score in log2
+ *                 units -- the softmax scale was applied there).
  *   v_mean        the same mean buffer given to vs_quantize_residual
  *                 ([B,H,nb,D] for VS_VMEAN_BLOCK, [B,H,D] for VS_VMEAN_SEQ),
  *                 NULL with VS_VMEAN_NONE.
@@ -152,11 +155,14 @@ int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
  *   lse2          out f32 [B,H,S]: log2 sum_t 2^(c * score_t) of the
  *                 (uncentred) logits: m + log2(l) + q_mu.
  * Non-causal full attention; keys past S are masked.  Per 128-key tile:
- * running max m' once per tile; P = E4M3(2^(s - m' + 8)) from an FP32
- * exp2, or with VS_EXPCAST the code rint(8 (s - m') + K0),
- * K0 = 120 - 4 (log2(1.5) - 1/2), codes < 8 -> 0; the tile row sum l_tile
- * is the sum of those E4M3 probabilities (formed on the FP8 matrix core);
- * O accumulates s_V * P.R~ + l_tile * mu_block.
+ * integer running max m' = max(m, ceil(max_t s_t)) once per tile;
+ * P = E4M3(2^(s - m' + 8)) (FP32 exp2 of s, offset by the power of two
+ * 2^(8 - m') in the FP8 conversion), or with VS_EXPCAST the code
+ * rint(8 (s - m') + K0), K0 = 120 - 4 (log2(1.5) - 1/2), codes < 8 -> 0;
+ * the tile row sum l_tile is the sum of those E4M3 probabilities (formed on
+ * the FP8 matrix core); O accumulates s_V * P.R~ + l_tile * mu_block, and is
+ * rescaled by the exact power of two 2^(m - m') when the max moves.
+ * Block scales must be powers of two (as vs_quantize_residual writes them).
  * S * D (rounded up to whole blocks) must stay below 2^31 per head
  * (VS_ERR_UNSUPPORTED otherwise).
  */
@@ -164,8 +170,7 @@ int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                     const float* k_scale, const uint8_t* v8,
                     const float* v_scale, const float* v_mean, int vmean_mode,
                     const float* q_mu, int B, int S, int H, int D,
-                    float softmax_scale, unsigned flags, float* out,
-                    float* lse2, void* stream);
+                    unsigned flags, float* out, float* lse2, void* stream);
 
 /*
  * vs_kmeans_permute -- V-Smooth grouping: integer k-means over each head's V

@@ -62,15 +62,14 @@ def test_attn_argument_errors(lib):
     fake = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
     args = lambda **kw: [kw.get("q8", fake), fake, fake, fake, fake, fake,  # noqa: E731
                          kw.get("vm", None), kw.get("mode", 0), None, kw.get("B", 1),
-                         kw.get("S", 256), 1, kw.get("D", 128), kw.get("scale", 0.1),
-                         kw.get("flags", 0), fake, fake, None]
+                         kw.get("S", 256), 1, kw.get("D", 128), kw.get("flags", 0), fake, fake,
+                         None]
     assert f(*args(D=96)) == 2
     assert f(*args(q8=None)) == 1
     assert f(*args(B=-1)) == 1
     assert f(*args(mode=1)) == 1                      # block mean without a buffer
     assert f(*args(mode=7, vm=fake)) == 1
     assert f(*args(flags=4)) == 1
-    assert f(*args(scale=0.0)) == 1
     assert f(*args(q8=ctypes.c_void_p(0x1004))) == 2  # misaligned
     assert f(*args(S=0)) == 0                         # empty problem
     assert f(*args(S=0, D=96)) == 2

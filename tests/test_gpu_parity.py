@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads
-from oracle import e4m3, pipeline
+from oracle import e4m3, pipeline, smoothing
 from gpu_util import (check_attn, check_intermediates, dev, oracle_head, plan_head,
                       run_plan)
 
@@ -92,7 +92,8 @@ def test_e4m3_conversion_at_rounding_boundaries():
     """A block whose amax is 448 has scale 1, so the codes are the E4M3
     rounding of the bf16 values themselves: every midpoint between
     neighbouring codes (ties to even), both neighbours of it, and values
-    beyond the subnormal range, through all three quantizers."""
+    beyond the subnormal range, through all three quantizers (Q with a
+    softmax scale whose score constant c is exactly 1)."""
     pos = e4m3.DECODE[:0x7F]
     mids = 0.5 * (pos[1:] + pos[:-1])
     vals = np.concatenate([pos, mids, -mids, -pos, np.nextafter(mids.astype(np.float32), np.inf),
@@ -107,7 +108,12 @@ def test_e4m3_conversion_at_rounding_boundaries():
     x[:len(vals)] = vals
     S = n // D
     t = torch.from_numpy(x.reshape(1, S, 1, D)).to(torch.bfloat16)
-    plan = run_plan(t, t, t, smooth=False)
+    L = smoothing.LOG2E_F32
+    s1 = [c for c in (np.float32(1.0 / float(L)), np.nextafter(np.float32(1.0 / float(L)), np.float32(1)),
+                      np.nextafter(np.float32(1.0 / float(L)), np.float32(0)))
+          if np.float32(c * L) == np.float32(1.0)][0]
+    assert smoothing.score_constant(s1) == np.float32(1.0)
+    plan = run_plan(t, t, t, smooth=False, softmax_scale=float(s1))
     want = e4m3.encode(x.reshape(S, D))
     np.testing.assert_array_equal(plan.q8[0, 0, :S].cpu().numpy(), want)
     np.testing.assert_array_equal(plan.k8[0, 0, :S].cpu().numpy(), want)
