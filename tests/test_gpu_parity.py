@@ -10,8 +10,8 @@ import torch
 
 import workloads
 from oracle import e4m3, pipeline, smoothing
-from gpu_util import (check_attn, check_intermediates, dev, oracle_head, plan_head,
-                      run_plan)
+from gpu_util import (attn_errors, check_attn, check_intermediates, dev, oracle_head,
+                      plan_head, run_plan)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +146,60 @@ def test_empty_problem_is_a_no_op():
     out, lse2 = plan.run(z, z, z)
     torch.cuda.synchronize(d)
     assert out.numel() == 0 and lse2.numel() == 0
+
+
+def _bf16(x):
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["max_above_64", "max_below_minus_64", "expcast_cap"])
+def test_extreme_score_ranges(case):
+    """Rows whose integer running max leaves [-64, 64] (the kernel's fallback
+    that forms exp2 of s + 8 - m instead of the scaled pack), and for ExpCast
+    rows with |m| >= 2^20 (the per-element cap at 126): same oracle, same bars.
+    The workloads never reach these branches."""
+    g = torch.Generator().manual_seed(11)
+    B, S, H, D = 1, 700, 2, 128
+    q = torch.randn(B, S, H, D, generator=g)
+    k = torch.randn(B, S, H, D, generator=g)
+    v = torch.randn(B, S, H, D, generator=g) + 0.5
+    smooth = True
+    if case == "max_above_64":
+        q = q * 40.0                     # scores ~ N(0, 57^2) in log2 units
+    elif case == "max_below_minus_64":
+        u = torch.randn(1, 1, H, D, generator=g)
+        k = u + 0.3 * k                  # keys share a direction ...
+        q = -8.0 * u + 0.5 * q           # ... that every query opposes
+        smooth = False                   # (centring would remove it)
+    else:
+        q = q * 3.0e5                    # |m| around 2^20 and beyond
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    rows = np.arange(0, S, 3)
+    for expcast in (False, True):
+        if case == "expcast_cap" and not expcast:
+            continue
+        plan = run_plan(q, k, v, smooth=smooth, expcast=expcast)
+        for h in range(H):
+            ref = oracle_head(q, k, v, 0, h, rows, smooth=smooth, expcast=expcast)
+            got = plan_head(plan, 0, h, rows)
+            check_intermediates(got, ref, S, label=f"{case} h{h}")
+            m_lo = float(np.min(ref["lse2"] - (ref["q_off"] if ref["q_off"] is not None else 0)))
+            m_hi = float(np.max(ref["lse2"] - (ref["q_off"] if ref["q_off"] is not None else 0)))
+            print(f"[{case}] expcast={expcast} h{h}: lse2 - qmu in [{m_lo:.1f}, {m_hi:.1f}]",
+                  flush=True)
+            if case == "max_above_64":
+                assert m_lo > 64
+            elif case == "max_below_minus_64":
+                assert m_hi < -64
+            else:
+                assert m_hi > 2.0 ** 20
+            if case == "expcast_cap":
+                # lse2 near 2^21 is a float32 with an ulp of 0.125-0.25: the
+                # 1e-4 bar becomes two ulps of the value there
+                e = attn_errors(got["O"], got["lse2"], ref)
+                assert e["max_abs"] <= 2e-3 and e["rel_l2"] <= 5e-3, e
+                ulp = np.spacing(np.abs(ref["lse2"]).astype(np.float32)).astype(np.float64)
+                d = np.abs(np.asarray(got["lse2"], np.float64) - ref["lse2"])
+                assert np.all(d <= np.maximum(1e-4, 2 * ulp)), float(d.max())
+            else:
+                check_attn(got["O"], got["lse2"], ref, label=f"{case} h{h} ec{expcast}")
