@@ -23,7 +23,8 @@
 //       32-key sub-tile; the power-of-two K and Q block scales are the E8M0
 //       operand scales, and Q carries softmax_scale * log2 e, so the product
 //       is the score in log2 units), then for tile j - 1: the row sum of its E4M3
-//       probabilities (P codes against an all-ones A operand), O^T +=
+//       probabilities (P codes as the B operand of two 16x16x128 products
+//       against a 0/1 A operand that keeps a lane's two queries apart), O^T +=
 //       2^e 2^-8 V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (the
 //       power-of-two V block scale and P's 2^8 are E8M0 operand scales, so
 //       the product accumulates straight into acc), and the rank-one restore
@@ -63,8 +64,9 @@ __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   return r;
 }
 
-__device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// 16x16x128 FP8 product without operand scales.
+__device__ __forceinline__ v4f mfma_fp8_16(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // E8M0 byte of a power-of-two float scale (its biased exponent).
@@ -127,7 +129,7 @@ struct Ctx {
   int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
   int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
   v8i qa[D / 64];                        // this lane's query, B operand of QK
-  v8i ones;                              // E4M3 ones, A operand of the row sums
+  v8i ones;                              // E4M3 ones or zeros, A operand of the row sums
 };
 
 // Recurrence state of one wave: log2-domain scores s of the current key
@@ -283,10 +285,16 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
       }
   }
   if (j >= 1) {
-    // row sums: P codes against E4M3 ones; every accumulator row holds the
-    // lane's query summed over the tile's 128 keys (both lane halves)
-    v16f rs = mfma_fp8(c.ones, st.pb[0], v16f{});
-    rs = mfma_fp8(c.ones, st.pb[1], rs);
+    // row sums on the 16x16x128 product, half the cost of a 32x32x64 one.
+    // Read as that shape, the P operand of one PV k-step holds in lane l
+    // column l % 16 and the 32 k values of lane group l / 16; those lanes
+    // carry query l % 32, i.e. column n pairs query n (groups 0 and 2)
+    // with query n + 16 (groups 1 and 3).  A row m of ones over the groups
+    // of parity (m / 4) % 2 only then sums one query, and the output row
+    // of lane l (4 (l / 16) + r) has that parity of l / 16: every lane's
+    // accumulator holds its own query's sum over the tile's 128 keys.
+    v4f rs = mfma_fp8_16(c.ones, st.pb[0], v4f{});
+    rs = mfma_fp8_16(c.ones, st.pb[1], rs);
     // O^T += 2^e 2^-8 V^T P^T: the E8M0 byte of the V block scale (a normal
     // power of two: its exponent field) and 2^-8 for P's prescale
     const int sv_e8 = (__float_as_int(st.vs) >> 23) & 0xFF;
@@ -482,7 +490,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     for (int e = 0; e < 2; ++e)
       c.v_rd[kk][e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c.ones[i] = 0x38383838;
+  for (int i = 0; i < 8; ++i)
+    c.ones[i] = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
 
   State<D> st;
   st.ks = c.ksc[0];
