@@ -10,9 +10,12 @@
 // permutation are the same on every run and every implementation:
 //   amax    grid (nb,H,B): per-head max |V| (bf16 magnitude bits, an integer
 //           max, combined with an integer atomic max)
-//   codes   grid (nb,H,B): codes = rint(V * 2^-e) as int8 [B,H,S,D], and a
-//           channel-major copy [B,H,D,S32] (S32 = S rounded up to 32, zero
-//           padded) through an LDS transpose, for the member-sum products
+//   codes   grid (nb,H,B): codes = rint(V * 2^-e) as int8 in two layouts of
+//           32-token blocks (S32 = S rounded up to 32, zero padded): token
+//           rows [B,H,S32/32,D/32,32,32] for the distance products and
+//           channel rows [B,H,S32/32,D,32] (an LDS transpose) for the
+//           member-sum products -- each 32 x 32-byte operand tile of a wave
+//           is then one contiguous 1 KB read
 //   init    grid (H,B): centroid j = codes of token floor(j*S/k)
 //   T x { assign grid (ceil(S/2048),H,B): distances |c|^2 - 2 v.c as int8
 //           matrix-core products (centroid tile x 32 tokens, exact int32),
@@ -43,8 +46,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct KmWs {
   uint32_t* amax;     // [B,H]
-  int8_t* codes;      // [B,H,S,D]
-  int8_t* codes_t;    // [B,H,D,S32]
+  int8_t* codes;      // [B,H,S32/32,D/32,32 tokens,32 channels]
+  int8_t* codes_t;    // [B,H,S32/32,D,32 tokens]
   int8_t* cent;       // [B,H,k,D]
   int32_t* psum;      // [B,H,nasg,k,D] partial member sums per assign chunk
   int32_t* pcnt;      // [B,H,nasg,k] partial member counts per assign chunk
@@ -65,7 +68,7 @@ size_t km_layout(int B, int S, int H, int D, int k, char* base, KmWs* ws) {
     return p;
   };
   char* a = take(bh * sizeof(uint32_t));
-  char* c = take(bh * S * D);
+  char* c = take(bh * D * static_cast<size_t>(round32(S)));
   char* ct = take(bh * D * static_cast<size_t>(round32(S)));
   char* ce = take(bh * k * D);
   char* ps = take(bh * nasg * k * D * sizeof(int32_t));
@@ -81,6 +84,16 @@ size_t km_layout(int B, int S, int H, int D, int k, char* base, KmWs* ws) {
     ws->chunk = reinterpret_cast<int32_t*>(ch);
   }
   return off;
+}
+
+// Byte offsets inside one head's codes (token rows) and channel-row copy.
+template <int D>
+__device__ __forceinline__ size_t xrow_off(int t, int d) {
+  return ((static_cast<size_t>(t >> 5) * (D / 32) + (d >> 5)) << 10) + ((t & 31) << 5) + (d & 31);
+}
+template <int D>
+__device__ __forceinline__ size_t xcol_off(int t, int d) {
+  return (static_cast<size_t>(t >> 5) * D + d) * 32 + (t & 31);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t val) {
@@ -145,6 +158,8 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
   const size_t bh = static_cast<size_t>(b) * H + h;
   const int S32 = round32(S);
   const double sc = ldexp(1.0, -code_exponent(amax[bh]));
+  int8_t* const xr = codes + bh * S32 * D;
+  int8_t* const xc = codes_t + bh * S32 * D;
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int row = r + ROWS * i, tok = j * kBlock + row;
@@ -159,18 +174,19 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
         out[e >> 1] |= ((static_cast<uint32_t>(lo) & 0xFFu) | ((static_cast<uint32_t>(hi) & 0xFFu) << 8))
                        << (16 * (e & 1));
       }
-      *reinterpret_cast<uint2*>(codes + (bh * S + tok) * D + 8 * c) = make_uint2(out[0], out[1]);
     }
-    // the transposed copy takes zeros for tokens past S
+    // tokens past S (up to S32) get zero codes in both layouts
+    if (tok < S32) *reinterpret_cast<uint2*>(xr + xrow_off<D>(tok, 8 * c)) = make_uint2(out[0], out[1]);
     *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c) = out[0];
     *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c + 4) = out[1];
   }
   __syncthreads();
-  // channel-major copy: 16-token chunks of one channel, 8 lanes per channel
-  // row (128 contiguous bytes of one row per 8 lanes)
+  // channel rows: per 32-token sub-block, D rows of 32 bytes; thread q
+  // writes 16 bytes, consecutive q consecutive in memory
   for (int q = threadIdx.x; q < D * (kBlock / 16); q += 256) {
-    const int d = q / (kBlock / 16), t0 = 16 * (q % (kBlock / 16));
-    if (j * kBlock + t0 >= S32) continue;
+    const int sub = q / (2 * D), d = (q >> 1) % D, t0 = 32 * sub + 16 * (q & 1);
+    const int tok0 = j * kBlock + t0;
+    if (tok0 >= S32) continue;
     uint32_t wv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -179,8 +195,7 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
       for (int u = 0; u < 4; ++u) x |= static_cast<uint32_t>(tile[(t0 + 4 * e + u) * TS + d]) << (8 * u);
       wv[e] = x;
     }
-    *reinterpret_cast<uint4*>(codes_t + (bh * D + d) * S32 + j * kBlock + t0) =
-        make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    *reinterpret_cast<uint4*>(xc + xcol_off<D>(tok0, d)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
 
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(256) void km_init_kernel(const int8_t* __restrict__
   for (int idx = threadIdx.x; idx < k * D; idx += blockDim.x) {
     const int jj = idx / D, d = idx % D;
     const long long src = (static_cast<long long>(jj) * S) / k;
-    cent[bh * k * D + idx] = codes[(bh * S + src) * D + d];
+    cent[bh * k * D + idx] = codes[bh * round32(S) * D + xrow_off<D>(static_cast<int>(src), d)];
   }
 }
 
@@ -224,7 +239,8 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
                                                         int32_t* __restrict__ pcnt) {
   constexpr int KS = D / 32;                // 32-channel k-steps
   constexpr int BPW = kAsg / 32 / 4;        // 32-token blocks per wave
-  __shared__ __attribute__((aligned(16))) int8_t scent[256 * D];
+  // centroids: ceil(k / 32) * 32 rows of D codes, sized at launch
+  extern __shared__ __attribute__((aligned(16))) int8_t scent[];
   __shared__ int32_t snorm[256];
   __shared__ int32_t scnt[256];
   __shared__ __attribute__((aligned(16))) uint8_t slab[kAsg];
@@ -239,6 +255,8 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
 
   const int4* gc = reinterpret_cast<const int4*>(cent + bh * k * D);
   for (int i = threadIdx.x; i < k * D / 16; i += 256) reinterpret_cast<int4*>(scent)[i] = gc[i];
+  for (int i = k * D / 16 + threadIdx.x; i < ntile * 32 * D / 16; i += 256)
+    reinterpret_cast<int4*>(scent)[i] = int4{0, 0, 0, 0};
   for (int i = threadIdx.x; i < 256; i += 256) scnt[i] = 0;
   for (int i = threadIdx.x; i < 32 * D; i += 256) sred[i] = 0;
   __syncthreads();
@@ -251,18 +269,28 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
   }
   __syncthreads();
 
+  // 32-token blocks of this wave that hold tokens (the rest of the chunk is
+  // past S); tokens past S inside a block have zero codes
+  const int tb0 = chunk * kAsg + wave * BPW * 32;
+  const int nblk = max(0, min(BPW, (S - tb0 + 31) / 32));
+  const int8_t* const xr = codes + bh * S32 * D;
+  const int8_t* const xc = codes_t + bh * S32 * D;
+
   // ---- labels ----
-  for (int i = 0; i < BPW; ++i) {
-    const int blk = wave * BPW + i;
-    const int tb = chunk * kAsg + blk * 32;
-    if (tb >= S) break;
-    const int tok = tb + l32;
-    const bool valid = tok < S;
-    v4i x[KS];
+  // operands of the next block are loaded while this one is processed
+  auto load_x = [&](int i, v4i (&x)[KS]) {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      x[s] = valid ? *reinterpret_cast<const v4i*>(codes + (bh * S + tok) * D + 32 * s + 16 * hh)
-                   : v4i{0, 0, 0, 0};
+      x[s] = *reinterpret_cast<const v4i*>(xr + xrow_off<D>(tb0 + 32 * i + l32, 32 * s + 16 * hh));
+  };
+  v4i x[KS];
+  if (nblk > 0) load_x(0, x);
+  for (int i = 0; i < nblk; ++i) {
+    const int blk = wave * BPW + i;
+    const int tok = tb0 + 32 * i + l32;
+    const bool valid = tok < S;
+    v4i xn[KS];
+    if (i + 1 < nblk) load_x(i + 1, xn);
     int best = 0x7FFFFFFF, bidx = 0;
     for (int ct = 0; ct < ntile; ++ct) {
       v16i dot = {};
@@ -295,30 +323,42 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
         atomicAdd(&scnt[bidx], 1);
       }
     }
+    if (i + 1 < nblk) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) x[s] = xn[s];
+    }
   }
   __syncthreads();
   for (int jj = threadIdx.x; jj < k; jj += 256)
     pcnt[(bh * nasg + chunk) * k + jj] = scnt[jj];
 
   // ---- member sums, one 32-centroid tile at a time ----
+  auto load_xt = [&](int i, v4i (&xt)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      xt[s] = *reinterpret_cast<const v4i*>(xc + xcol_off<D>(tb0 + 32 * i + 16 * hh, 32 * s + l32));
+  };
   for (int ct = 0; ct < ntile; ++ct) {
     v16i acc[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc[s] = v16i{};
     const uint32_t cid = static_cast<uint32_t>(ct * 32 + l32) * 0x01010101u;
-    for (int i = 0; i < BPW; ++i) {
+    v4i xt[KS];
+    if (nblk > 0) load_xt(0, xt);
+    for (int i = 0; i < nblk; ++i) {
       const int blk = wave * BPW + i;
-      const int tb = chunk * kAsg + blk * 32;
-      if (tb >= S) break;
+      v4i xtn[KS];
+      if (i + 1 < nblk) load_xt(i + 1, xtn);
       const uint4 lb = *reinterpret_cast<const uint4*>(slab + blk * 32 + 16 * hh);
       const v4i oh = {static_cast<int>(zero_bytes_to_ones(lb.x ^ cid)),
                       static_cast<int>(zero_bytes_to_ones(lb.y ^ cid)),
                       static_cast<int>(zero_bytes_to_ones(lb.z ^ cid)),
                       static_cast<int>(zero_bytes_to_ones(lb.w ^ cid))};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const v4i xt = *reinterpret_cast<const v4i*>(codes_t + (bh * D + 32 * s + l32) * S32 + tb + 16 * hh);
-        acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oh, xt, acc[s], 0, 0, 0);
+      for (int s = 0; s < KS; ++s) acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oh, xt[s], acc[s], 0, 0, 0);
+      if (i + 1 < nblk) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) xt[s] = xtn[s];
       }
     }
     // lane holds channel 32 s + l32 of centroids 8 (r / 4) + 4 hh + r % 4
@@ -466,7 +506,8 @@ void run_kmeans(const uint16_t* k, const uint16_t* v, int B, int S, int H, int k
   hipLaunchKernelGGL(km_init_kernel<D>, dim3(H, B), dim3(256), 0, st, ws.codes, S, H, kc, ws.cent);
   const int nasg = (S + kAsg - 1) / kAsg;
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(km_assign_kernel<D>, dim3(nasg, H, B), dim3(256), 0, st, ws.codes,
+    hipLaunchKernelGGL(km_assign_kernel<D>, dim3(nasg, H, B), dim3(256),
+                       static_cast<unsigned>((kc + 31) / 32 * 32 * D), st, ws.codes,
                        ws.codes_t, S, H, kc, ws.cent, labels, ws.psum, ws.pcnt);
     hipLaunchKernelGGL(km_update_kernel<D>, dim3((kc * D + 255) / 256, H, B), dim3(256), 0, st, H,
                        kc, nasg, ws.cent, ws.psum, ws.pcnt);

@@ -148,62 +148,108 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
 }
 
+// Columns k of the 4x4 byte matrix whose rows are w[0..3]: byte k of the
+// result e is byte e of w[k] (two rounds of v_perm_b32).
+__device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&col)[4]) {
+  const uint32_t x0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+  const uint32_t x1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+  const uint32_t y0 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const uint32_t y1 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  col[0] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
+  col[1] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
+  col[2] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+  col[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+}
+
 // Residual V: codes transposed per block, [D][128] in the MFMA token order,
-// power-of-two scale.
+// power-of-two scale.  Thread t owns channels 8 (t % CH) .. + 7 and whole
+// token quads 4a .. 4a + 3: v_pos keeps a quad's four tokens in one aligned
+// dword, so a byte transpose in registers yields one dword per channel and
+// quad.  The LDS tile is XOR-swizzled by 16-byte chunk (chunk ^ (d / 8) % 8
+// in row d) so the dword writes of a wave, whose rows d are 1 KB apart,
+// spread over the banks; the copy-out reads it back in row order.
 template <int D>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out) {
-  constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
+  constexpr int CH = D / 8;              // 8-channel groups
+  constexpr int QR = 256 / CH;           // quads in flight per pass
+  constexpr int NQ = kBlock / 4 / QR;    // quads per thread
   __shared__ float red4[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlock];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int c = threadIdx.x % CH, r = threadIdx.x / CH;
+  const int c = threadIdx.x % CH, a0 = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
-  const float* mean8 = nullptr;
-  if (vmean_mode == VS_VMEAN_BLOCK) mean8 = v_mean + (bh * nb + j) * D + 8 * c;
-  else if (vmean_mode == VS_VMEAN_SEQ) mean8 = v_mean + bh * D + 8 * c;
+  float mu[8];
+  {
+    const float* mean8 = nullptr;
+    if (vmean_mode == VS_VMEAN_BLOCK) mean8 = v_mean + (bh * nb + j) * D + 8 * c;
+    else if (vmean_mode == VS_VMEAN_SEQ) mean8 = v_mean + bh * D + 8 * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = mean8 ? mean8[e] : 0.0f;
+  }
 
-  float val[TPT][8];
-  load_block<D>(x, layout, b, h, j, S, H, mean8, val);
+  // residuals in float32; padding tokens are +0
+  float val[NQ][4][8];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tok = j * kBlock + 4 * (a0 + QR * n) + q;
+      if (tok < S) {
+        const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, tok, h, S, H, D) + 8 * c);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          val[n][q][2 * e] = bf16_to_f32(ww[e] & 0xFFFFu) - mu[2 * e];
+          val[n][q][2 * e + 1] = bf16_to_f32(ww[e] >> 16) - mu[2 * e + 1];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) val[n][q][e] = 0.0f;
+      }
+    }
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int tok = j * kBlock + r + ROWS * i;
-    if (tok < S) {
+  for (int n = 0; n < NQ; ++n)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(val[i][e]));
-    }
-  }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(val[n][q][e]));
   const float amax = block_amax(a, red4);
   const int e = pow2_exponent(amax);
   const float inv = ldexpf(1.0f, -e);
   if (threadIdx.x == 0) scale_out[bh * nb + j] = ldexpf(1.0f, e);
 
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int tau = r + ROWS * i;            // token inside the block
-    const int tok = j * kBlock + tau;
-    uint32_t w0 = 0, w1 = 0;
-    if (tok < S) {
-      w0 = cvt_pk_e4m3<false>(clamp448(val[i][0] * inv), clamp448(val[i][1] * inv), w0);
-      w0 = cvt_pk_e4m3<true>(clamp448(val[i][2] * inv), clamp448(val[i][3] * inv), w0);
-      w1 = cvt_pk_e4m3<false>(clamp448(val[i][4] * inv), clamp448(val[i][5] * inv), w1);
-      w1 = cvt_pk_e4m3<true>(clamp448(val[i][6] * inv), clamp448(val[i][7] * inv), w1);
-    }
-    const int p = v_pos(tau);
+  for (int n = 0; n < NQ; ++n) {
+    uint32_t lo[4], hi[4];                 // token q: channels 0-3, 4-7
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[(8 * c + e) * kBlock + p] = static_cast<uint8_t>(w0 >> (8 * e));
-      tile[(8 * c + 4 + e) * kBlock + p] = static_cast<uint8_t>(w1 >> (8 * e));
+    for (int q = 0; q < 4; ++q) {
+      const float* v = val[n][q];
+      lo[q] = cvt_pk_e4m3<false>(clamp448(v[0] * inv), clamp448(v[1] * inv), 0u);
+      lo[q] = cvt_pk_e4m3<true>(clamp448(v[2] * inv), clamp448(v[3] * inv), lo[q]);
+      hi[q] = cvt_pk_e4m3<false>(clamp448(v[4] * inv), clamp448(v[5] * inv), 0u);
+      hi[q] = cvt_pk_e4m3<true>(clamp448(v[6] * inv), clamp448(v[7] * inv), hi[q]);
     }
+    uint32_t col[8];                       // channel e: the quad's 4 tokens
+    transpose4x4(lo, *reinterpret_cast<uint32_t(*)[4]>(col));
+    transpose4x4(hi, *reinterpret_cast<uint32_t(*)[4]>(col + 4));
+    const int p = v_pos(4 * (a0 + QR * n));  // byte of token 4a (a multiple of 4)
+    const int swz = ((p >> 4) ^ (c & 7)) << 4 | (p & 15);
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2)
+      *reinterpret_cast<uint32_t*>(tile + (8 * c + e2) * kBlock + swz) = col[e2];
   }
   __syncthreads();
   uint4* dst = reinterpret_cast<uint4*>(codes + (bh * nb + j) * static_cast<size_t>(D) * kBlock);
-  const uint4* src = reinterpret_cast<const uint4*>(tile);
 #pragma unroll
-  for (int i = 0; i < D * kBlock / 16 / 256; ++i) dst[threadIdx.x + 256 * i] = src[threadIdx.x + 256 * i];
+  for (int i = 0; i < D * kBlock / 16 / 256; ++i) {
+    const int idx = threadIdx.x + 256 * i;   // 16-byte chunk of the row-major tile
+    const int row = idx >> 3, ch = idx & 7;
+    dst[idx] = *reinterpret_cast<const uint4*>(tile + row * kBlock + ((ch ^ ((row >> 3) & 7)) << 4));
+  }
 }
 
 }  // namespace
