@@ -1,16 +1,20 @@
 """Accuracy of the smoothed FP8 path against FP64 dense attention, next to
 the unsmoothed FP8 path, at the five workloads' full sizes (TeleFuser PR
 #40, "Smooth Attention Kernel Accuracy": smoothing lowers the attention
-output error).  Reported per workload and head: relative L2 (and MSE) of O
-with smoothing on and off.  Asserted: both are finite and small, and for
-the workloads whose K carries a large per-channel offset (the case K
-centring targets) smoothing lowers the error."""
+output error).  Reported per workload and head: relative L2, MSE, cosine
+and SQNR of O with smoothing on and off; for the ExpCast workload also the
+smoothed path with ExpCast off; for the grouped workloads the share of V
+energy the block means remove, in sequence order and in k-means order
+(VC-Attention summary, Main Findings), from the oracle's own grouping.
+Asserted: both errors are finite and small, for the workloads whose K
+carries a large per-channel offset (the case K centring targets) smoothing
+lowers the error, and grouping raises the removed energy."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from oracle import attention, pipeline
+from oracle import attention, kmeans, pipeline
 from gpu_util import dev
 
 pytestmark = pytest.mark.gpu
@@ -19,11 +23,12 @@ pytestmark = pytest.mark.gpu
 OFFSET_K = {"tiny", "mid"}
 
 
-def _outputs(w, q, k, v, smooth):
+def _outputs(w, q, k, v, smooth, expcast=None):
     import bit_attention_video_smooth_amd as vs
     d = dev()
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, smooth=smooth,
-                   kmeans=w.kmeans if smooth else None, expcast=w.expcast)
+                   kmeans=w.kmeans if smooth else None,
+                   expcast=w.expcast if expcast is None else expcast)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     return plan.out
@@ -36,25 +41,39 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
     print(f"[accuracy] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={w.expcast}",
           flush=True)
     q, k, v = workloads.generate(w, device=d)
-    outs = {s: _outputs(w, q, k, v, s) for s in (True, False)}
+    cases = {"smoothed": _outputs(w, q, k, v, True), "unsmoothed": _outputs(w, q, k, v, False)}
+    if w.expcast:
+        cases["smoothed, ExpCast off"] = _outputs(w, q, k, v, True, expcast=False)
     rows = pipeline.sample_rows(w.S, 32)
     scale = pipeline.default_scale(w.D)
-    errs = {True: [], False: []}
+    errs = {c: [] for c in cases}
+    energy = {"sequence": [], "k-means": []}
     for h in sorted({0, w.H // 2, w.H - 1}):
         qh, kh, vh = workloads.head_slices(q, k, v, 0, h)
         ref, _ = attention.dense_attention(qh[rows], kh, vh, scale)
-        line = [f"[accuracy] {name} h{h}"]
-        for s in (True, False):
-            o = outs[s][0, :, h, :].cpu().numpy()[rows]
+        for c, out in cases.items():
+            o = out[0, :, h, :].cpu().numpy()[rows]
             assert np.isfinite(o).all()
             e = pipeline.error_report(o, ref)
-            errs[s].append(e["rel_l2"])
-            line.append(f"{'smoothed' if s else 'unsmoothed'} rel_l2 {e['rel_l2']:.4e} "
-                        f"mse {e['mse']:.4e}")
-        print("  ".join(line), flush=True)
-    sm, un = float(np.mean(errs[True])), float(np.mean(errs[False]))
-    print(f"[accuracy] {name} mean rel_l2: smoothed {sm:.4e} unsmoothed {un:.4e} "
-          f"ratio {sm / un:.3f}", flush=True)
+            errs[c].append(e)
+            print(f"[accuracy] {name} h{h} {c}: rel_l2 {e['rel_l2']:.4e} mse {e['mse']:.4e} "
+                  f"cos {e['cos']:.8f} sqnr {e['sqnr_db']:.2f} dB", flush=True)
+        if w.kmeans is not None:
+            _, _, _, vp = kmeans.kmeans_permute_head(kh, vh, *w.kmeans)
+            energy["sequence"].append(kmeans.block_energy_removed(vh))
+            energy["k-means"].append(kmeans.block_energy_removed(vp))
+    mean = {c: {m: float(np.mean([e[m] for e in errs[c]])) for m in ("rel_l2", "mse", "cos", "sqnr_db")}
+            for c in cases}
+    for c, m in mean.items():
+        print(f"[accuracy] {name} mean over heads, {c}: rel_l2 {m['rel_l2']:.4e} mse {m['mse']:.4e} "
+              f"cos {m['cos']:.8f} sqnr {m['sqnr_db']:.2f} dB", flush=True)
+    sm, un = mean["smoothed"]["rel_l2"], mean["unsmoothed"]["rel_l2"]
+    print(f"[accuracy] {name} rel_l2 ratio smoothed/unsmoothed {sm / un:.3f}", flush=True)
     assert sm < 0.1 and un < 0.5
     if name in OFFSET_K:
         assert sm < un
+    if w.kmeans is not None:
+        es, ek = float(np.mean(energy["sequence"])), float(np.mean(energy["k-means"]))
+        print(f"[accuracy] {name} V energy removed by the block means: sequence order {es:.4f}, "
+              f"k-means order {ek:.4f}", flush=True)
+        assert ek > es
