@@ -8,4 +8,4 @@ from .api import (Plan, attention, vs_fp8_attn_fwd, vs_kmeans_permute,  # noqa: 
                   vs_kmeans_workspace_bytes, vs_quantize_residual, vs_smooth_stats,
                   vs_smooth_stats_workspace_bytes, vs_version)
 from ._abi import (VS_EXPCAST, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,  # noqa: F401
-                   VS_VMEAN_NONE, VS_VMEAN_SEQ, VsError, LIB_PATH)
+                   VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, VsError, LIB_PATH)

@@ -7,7 +7,7 @@ LIB_PATH = os.path.join(HERE, "libvsmooth.so")
 
 VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = range(5)
 VS_LAYOUT_BSHD, VS_LAYOUT_BHSD = 0, 1
-VS_VMEAN_NONE, VS_VMEAN_BLOCK, VS_VMEAN_SEQ = 0, 1, 2
+VS_VMEAN_NONE, VS_VMEAN_BLOCK, VS_VMEAN_SEQ, VS_VMEAN_BLOCK_OUT = 0, 1, 2, 3
 VS_EXPCAST = 1
 
 _P = ctypes.c_void_p

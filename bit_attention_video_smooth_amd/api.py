@@ -16,7 +16,7 @@ import torch
 
 from . import _abi
 from ._abi import (VS_EXPCAST, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
-                   VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
+                   VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
            "vs_fp8_attn_fwd", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
@@ -153,12 +153,17 @@ class Plan:
             vs_kmeans_permute(k, v, shape, kc, iters, self.labels, self.perm, self.k_perm,
                               self.v_perm, self.km_ws)
             kk, vv, layout = self.k_perm, self.v_perm, VS_LAYOUT_BHSD
+        qmode = self.vmean_mode
         if self.smooth:
-            blk = self.v_mean if self.vmean_mode == VS_VMEAN_BLOCK else None
+            # block means come out of the V quantizer (VS_VMEAN_BLOCK_OUT), so
+            # the statistics pass reads K only; the sequence mean needs V here
             seq = self.v_mean if self.vmean_mode == VS_VMEAN_SEQ else None
-            vs_smooth_stats(kk, vv, shape, layout, self.k_mean, blk, seq, self.stats_ws)
+            vs_smooth_stats(kk, vv if seq is not None else None, shape, layout, self.k_mean, None,
+                            seq, self.stats_ws)
+            if self.vmean_mode == VS_VMEAN_BLOCK:
+                qmode = VS_VMEAN_BLOCK_OUT
         vs_quantize_residual(q, kk, vv, layout, shape, self.softmax_scale, self.k_mean,
-                             self.v_mean, self.vmean_mode, self.q8, self.q_scale, self.k8,
+                             self.v_mean, qmode, self.q8, self.q_scale, self.k8,
                              self.k_scale, self.v8, self.v_scale, self.q_mu)
         self.attn()
         return self.out, self.lse2

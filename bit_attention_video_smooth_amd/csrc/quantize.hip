@@ -168,23 +168,31 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
 // quad.  The LDS tile is XOR-swizzled by 16-byte chunk (chunk ^ (d / 8) % 8
 // in row d) so the dword writes of a wave, whose rows d are 1 KB apart,
 // spread over the banks; the copy-out reads it back in row order.
-template <int D>
+//
+// OWN_MEAN (mode VS_VMEAN_BLOCK_OUT): the block mean is formed here from the
+// values already in registers -- float64 sums of the bf16 values (exact),
+// per thread, then over the threads of a channel group in a fixed order, one
+// division, one rounding to float32, as vs_smooth_stats forms it -- written
+// to v_mean and subtracted.
+template <int D, bool OWN_MEAN>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
-    const float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
+    float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out) {
   constexpr int CH = D / 8;              // 8-channel groups
   constexpr int QR = 256 / CH;           // quads in flight per pass
   constexpr int NQ = kBlock / 4 / QR;    // quads per thread
   __shared__ float red4[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlock];
+  __shared__ double part[OWN_MEAN ? QR : 1][OWN_MEAN ? D : 1];
+  __shared__ float smean[OWN_MEAN ? D : 1];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int c = threadIdx.x % CH, a0 = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
   float mu[8];
   {
     const float* mean8 = nullptr;
-    if (vmean_mode == VS_VMEAN_BLOCK) mean8 = v_mean + (bh * nb + j) * D + 8 * c;
+    if (!OWN_MEAN && vmean_mode == VS_VMEAN_BLOCK) mean8 = v_mean + (bh * nb + j) * D + 8 * c;
     else if (vmean_mode == VS_VMEAN_SEQ) mean8 = v_mean + bh * D + 8 * c;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mu[e] = mean8 ? mean8[e] : 0.0f;
@@ -210,6 +218,35 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
         for (int e = 0; e < 8; ++e) val[n][q][e] = 0.0f;
       }
     }
+  if (OWN_MEAN) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double sum = 0.0;
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum += static_cast<double>(val[n][q][e]);
+      part[a0][8 * c + e] = sum;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+      double sum = 0.0;
+      for (int r = 0; r < QR; ++r) sum += part[r][threadIdx.x];
+      const float m = static_cast<float>(sum / static_cast<double>(min(kBlock, S - j * kBlock)));
+      smean[threadIdx.x] = m;
+      v_mean[(bh * nb + j) * D + threadIdx.x] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float m = smean[8 * c + e];
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j * kBlock + 4 * (a0 + QR * n) + q < S) val[n][q][e] -= m;
+    }
+  }
   float a = 0.0f;
 #pragma unroll
   for (int n = 0; n < NQ; ++n)
@@ -258,13 +295,14 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
 extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     int kv_layout, int B, int S, int H, int D,
                                     float softmax_scale, const float* k_mean,
-                                    const float* v_mean, int vmean_mode, uint8_t* q8,
+                                    float* v_mean, int vmean_mode, uint8_t* q8,
                                     float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8,
                                     float* v_scale, float* q_mu, void* stream) {
   using namespace vs;
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
-  if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
+  if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
+      vmean_mode != VS_VMEAN_BLOCK_OUT)
     return VS_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !(softmax_scale <= FLT_MAX)) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
@@ -287,15 +325,23 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
                        nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
     hipLaunchKernelGGL(quant_rows_kernel<128>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
                        1.0f, k8, k_scale, nullptr, nullptr, c_log2);
-    hipLaunchKernelGGL(quant_vt_kernel<128>, grid, block, 0, st, v, kv_layout, S, H, nb, v_mean,
-                       vmean_mode, v8, v_scale);
+    if (vmean_mode == VS_VMEAN_BLOCK_OUT)
+      hipLaunchKernelGGL((quant_vt_kernel<128, true>), grid, block, 0, st, v, kv_layout, S, H, nb,
+                         v_mean, vmean_mode, v8, v_scale);
+    else
+      hipLaunchKernelGGL((quant_vt_kernel<128, false>), grid, block, 0, st, v, kv_layout, S, H, nb,
+                         v_mean, vmean_mode, v8, v_scale);
   } else {
     hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
                        nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
     hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
                        1.0f, k8, k_scale, nullptr, nullptr, c_log2);
-    hipLaunchKernelGGL(quant_vt_kernel<64>, grid, block, 0, st, v, kv_layout, S, H, nb, v_mean,
-                       vmean_mode, v8, v_scale);
+    if (vmean_mode == VS_VMEAN_BLOCK_OUT)
+      hipLaunchKernelGGL((quant_vt_kernel<64, true>), grid, block, 0, st, v, kv_layout, S, H, nb,
+                         v_mean, vmean_mode, v8, v_scale);
+    else
+      hipLaunchKernelGGL((quant_vt_kernel<64, false>), grid, block, 0, st, v, kv_layout, S, H, nb,
+                         v_mean, vmean_mode, v8, v_scale);
   }
   return launch_status();
 }

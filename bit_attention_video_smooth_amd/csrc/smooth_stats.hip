@@ -8,7 +8,8 @@
 //   stage 1, grid (nb, H, B): one workgroup per 128-token block sums K and V
 //     over its valid tokens in float64 (a bf16 value has 8 significant bits,
 //     so these sums are exact), writes the block mean of V and keeps the two
-//     block sums in the workspace.
+//     block sums in the workspace.  With no V output requested V is not
+//     read (v == nullptr).
 //   stage 2, grid (H, B): sums the nb block sums in a fixed order and writes
 //     the sequence means.  Fixed orders make the result deterministic.
 //
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void stats_block_kernel(
     if (tok < S) {
       const size_t off = token_offset(layout, b, tok, h, S, H, D) + 8 * c;
       const uint4 kk = *reinterpret_cast<const uint4*>(k + off);
-      const uint4 vv = *reinterpret_cast<const uint4*>(v + off);
+      const uint4 vv = v ? *reinterpret_cast<const uint4*>(v + off) : uint4{0u, 0u, 0u, 0u};
       const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(256) void stats_block_kernel(
     for (int rr = 0; rr < ROWS; ++rr) s += red[rr][threadIdx.x];
     ws_k[out + threadIdx.x] = s;
   }
+  if (!v) return;
   __syncthreads();
   // V block sums and block means
 #pragma unroll
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(1024) void stats_seq_kernel(
   double sk = 0.0, sv = 0.0;
   for (int j = g; j < nb; j += G) {
     sk += ws_k[base + static_cast<size_t>(j) * D + d];
-    sv += ws_v[base + static_cast<size_t>(j) * D + d];
+    if (v_seq_mean) sv += ws_v[base + static_cast<size_t>(j) * D + d];
   }
   part[0][g][d] = sk;
   part[1][g][d] = sv;
@@ -132,8 +134,8 @@ extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int 
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if (!k_mean && !v_block_mean && !v_seq_mean) return VS_ERR_INVALID_ARG;
-  if (!k || !v) return VS_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned16(v) || (k_mean && !aligned16(k_mean)) ||
+  if (!k || (!v && (v_block_mean || v_seq_mean))) return VS_ERR_INVALID_ARG;
+  if (!aligned16(k) || (v && !aligned16(v)) || (k_mean && !aligned16(k_mean)) ||
       (v_block_mean && !aligned16(v_block_mean)) || (v_seq_mean && !aligned16(v_seq_mean)))
     return VS_ERR_UNSUPPORTED;
   const size_t need = ws_bytes_needed(B, S, H, D);

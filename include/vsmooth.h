@@ -62,6 +62,9 @@ extern "C" {
 #define VS_VMEAN_NONE  0        /* V quantized as is, nothing restored       */
 #define VS_VMEAN_BLOCK 1        /* per-128-block mean, restored per tile     */
 #define VS_VMEAN_SEQ   2        /* one sequence mean, restored at the end    */
+#define VS_VMEAN_BLOCK_OUT 3    /* vs_quantize_residual only: forms the      */
+                                /* per-block means itself and writes them;   */
+                                /* attention then takes VS_VMEAN_BLOCK       */
 
 /* vs_fp8_attn_fwd flags */
 #define VS_EXPCAST 1u           /* ExpCast-FP8 probability cast              */
@@ -79,7 +82,8 @@ const char* vs_version(void);
  * VC-Attention summary, Key Contribution 1 (per-block V mean).
  *
  *   k, v          bf16 [B,S,H,D] (layout VS_LAYOUT_BSHD) or [B,H,S,D]
- *                 (VS_LAYOUT_BHSD), e.g. the permuted K', V'.
+ *                 (VS_LAYOUT_BHSD), e.g. the permuted K', V'.  v may be
+ *                 NULL when both V outputs are NULL (then V is not read).
  *   k_mean        out f32 [B,H,D]: mean of K over the S tokens, or NULL.
  *   v_block_mean  out f32 [B,H,nb,D]: mean of V over each block's valid
  *                 tokens, or NULL.
@@ -107,7 +111,11 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
  *                 its quantization, and q_mu uses the same c.
  *   k_mean        f32 [B,H,D] from vs_smooth_stats, or NULL: no K centring.
  *   v_mean        f32 [B,H,nb,D] (VS_VMEAN_BLOCK) or [B,H,D] (VS_VMEAN_SEQ),
- *                 or NULL with VS_VMEAN_NONE.
+ *                 read; or out f32 [B,H,nb,D] (VS_VMEAN_BLOCK_OUT): each
+ *                 block's mean over its valid tokens, formed here from the
+ *                 same V the block quantizer reads, exactly as
+ *                 vs_smooth_stats forms v_block_mean (bit-identical), which
+ *                 saves that call's pass over V; NULL with VS_VMEAN_NONE.
  *   q8, k8        out u8 [B,H,S_pad,D]: E4M3 codes, row per token.
  *   v8            out u8 [B,H,nb,D,128]: E4M3 codes of the residual, per
  *                 block one row of 128 tokens per channel.  Within a block
@@ -129,7 +137,7 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
 int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, int kv_layout, int B, int S, int H,
                          int D, float softmax_scale, const float* k_mean,
-                         const float* v_mean, int vmean_mode, uint8_t* q8,
+                         float* v_mean, int vmean_mode, uint8_t* q8,
                          float* q_scale, uint8_t* k8, float* k_scale,
                          uint8_t* v8, float* v_scale, float* q_mu,
                          void* stream);

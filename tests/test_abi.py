@@ -86,13 +86,28 @@ def test_quant_stats_kmeans_argument_errors(lib):
     assert q(*bad) == 1                                # k_mean without q_mu
     bad = list(base); bad[11] = 1
     assert q(*bad) == 1                                # vmean block without buffer
+    bad = list(base); bad[11] = 3
+    assert q(*bad) == 1                                # block means out without buffer
+    bad = list(base); bad[11] = 4; bad[10] = fake
+    assert q(*bad) == 1                                # no such mode
     bad = list(base); bad[7] = 32
     assert q(*bad) == 2
     s = lib.vs_smooth_stats
     assert s(fake, fake, 1, 300, 2, 128, 0, None, None, None, fake, 1 << 30, None) == 1
+    assert s(fake, None, 1, 300, 2, 128, 0, fake, fake, None, fake, 1 << 30, None) == 1  # V mean, no V
+    assert s(fake, None, 1, 300, 2, 128, 0, fake, None, fake, fake, 1 << 30, None) == 1
     assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, fake, 16, None) == 3
     assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, None, 1 << 30, None) == 3
     k = lib.vs_kmeans_permute
     assert k(fake, fake, 1, 300, 2, 128, 16, 0, fake, fake, fake, fake, fake, 1 << 30, None) == 1
     assert k(fake, fake, 1, 300, 2, 128, 300, 2, fake, fake, fake, fake, fake, 1 << 30, None) == 2
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, fake, fake, 64, None) == 3
+
+
+def test_header_constants_match_the_binding():
+    from bit_attention_video_smooth_amd import _abi
+    text = open(HEADER).read()
+    for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
+                 "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD"]:
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(_abi, name), name

@@ -203,3 +203,60 @@ def test_extreme_score_ranges(case):
                 assert np.all(d <= np.maximum(1e-4, 2 * ulp)), float(d.max())
             else:
                 check_attn(got["O"], got["lse2"], ref, label=f"{case} h{h} ec{expcast}")
+
+
+@pytest.mark.parametrize("S,D,layout", [(300, 128, "bshd"), (8192, 128, "bhsd"), (1000, 64, "bshd")])
+def test_block_means_from_the_quantizer_equal_the_statistics_pass(S, D, layout):
+    """VS_VMEAN_BLOCK_OUT (block means formed by the V quantizer, statistics
+    pass over K only) against vs_smooth_stats' block means fed to the
+    quantizer as VS_VMEAN_BLOCK: the means, codes and scales are
+    bit-identical, and the means equal the oracle's."""
+    import bit_attention_video_smooth_amd as vs
+    from bit_attention_video_smooth_amd import api
+    d = dev()
+    B, H = 2, 3
+    g = torch.Generator().manual_seed(S + D)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    k = (torch.randn(B, S, H, D, generator=g) + 2.0).to(torch.bfloat16)
+    v = (torch.randn(B, S, H, D, generator=g) * 3.0 + 1.5).to(torch.bfloat16)
+    lay = vs.VS_LAYOUT_BSHD
+    kk, vv = k, v
+    if layout == "bhsd":
+        lay = vs.VS_LAYOUT_BHSD
+        kk, vv = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+    qd, kd, vd = q.to(d), kk.to(d), vv.to(d)
+    shape = (B, S, H, D)
+    nb = (S + 127) // 128
+    f32, u8 = torch.float32, torch.uint8
+    ws = torch.empty(api.vs_smooth_stats_workspace_bytes(B, S, H, D), dtype=u8, device=d)
+
+    def outs():
+        return dict(q8=torch.empty(B, H, nb * 128, D, dtype=u8, device=d),
+                    k8=torch.empty(B, H, nb * 128, D, dtype=u8, device=d),
+                    v8=torch.empty(B, H, nb, D, 128, dtype=u8, device=d),
+                    qs=torch.empty(B, H, nb, dtype=f32, device=d),
+                    ks=torch.empty(B, H, nb, dtype=f32, device=d),
+                    vs_=torch.empty(B, H, nb, dtype=f32, device=d),
+                    vm=torch.full((B, H, nb, D), float("nan"), dtype=f32, device=d),
+                    km=torch.empty(B, H, D, dtype=f32, device=d),
+                    qmu=torch.empty(B, H, S, dtype=f32, device=d))
+
+    sep, fus = outs(), outs()
+    api.vs_smooth_stats(kd, vd, shape, lay, sep["km"], sep["vm"], None, ws)
+    api.vs_quantize_residual(qd, kd, vd, lay, shape, 0.088, sep["km"], sep["vm"],
+                             vs.VS_VMEAN_BLOCK, sep["q8"], sep["qs"], sep["k8"], sep["ks"],
+                             sep["v8"], sep["vs_"], sep["qmu"])
+    api.vs_smooth_stats(kd, None, shape, lay, fus["km"], None, None, ws)
+    api.vs_quantize_residual(qd, kd, vd, lay, shape, 0.088, fus["km"], fus["vm"],
+                             vs.VS_VMEAN_BLOCK_OUT, fus["q8"], fus["qs"], fus["k8"], fus["ks"],
+                             fus["v8"], fus["vs_"], fus["qmu"])
+    torch.cuda.synchronize(d)
+    for name in sep:
+        a, b = sep[name], fus[name]
+        if a.dtype == f32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
+        assert torch.equal(a, b), name
+    for b_ in range(B):
+        for h in range(H):
+            want = smoothing.v_block_means(v[b_, :, h, :].float().numpy())
+            np.testing.assert_array_equal(fus["vm"][b_, h].cpu().numpy(), want)
