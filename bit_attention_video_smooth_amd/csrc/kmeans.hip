@@ -104,10 +104,14 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t val) {
 
 template <int D>
 __global__ __launch_bounds__(256) void km_amax_kernel(const uint16_t* __restrict__ v, int S,
-                                                      int H, uint32_t* __restrict__ amax) {
+                                                      int H, uint32_t* __restrict__ amax,
+                                                      int hfast) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   __shared__ uint32_t red[4];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the head is the fastest grid index (V is token-major): workgroups that
+  // run together read neighbouring pieces of the same token rows
+  const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
+            b = blockIdx.z;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
   uint32_t mx = 0;
 #pragma unroll
@@ -149,11 +153,15 @@ template <int D>
 __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restrict__ v, int S,
                                                        int H, const uint32_t* __restrict__ amax,
                                                        int8_t* __restrict__ codes,
-                                                       int8_t* __restrict__ codes_t) {
+                                                       int8_t* __restrict__ codes_t,
+                                                       int hfast) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   constexpr int TS = D + 4;                 // LDS row stride (bytes): fewer bank conflicts
   __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * TS];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the head is the fastest grid index (V is token-major): workgroups that
+  // run together read neighbouring pieces of the same token rows
+  const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
+            b = blockIdx.z;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const int S32 = round32(S);
@@ -500,9 +508,14 @@ void run_kmeans(const uint16_t* k, const uint16_t* v, int B, int S, int H, int k
   const size_t bh = static_cast<size_t>(B) * H;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((bh + 255) / 256, 1024))),
                      dim3(256), 0, st, ws.amax, bh, 0u);
-  hipLaunchKernelGGL(km_amax_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax);
-  hipLaunchKernelGGL(km_codes_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax, ws.codes,
-                     ws.codes_t);
+  // the amax pass only reads V: head-fastest order (neighbouring pieces of
+  // the same token rows) measured 28-34% faster; the codes pass, whose
+  // writes go to head-major layouts, runs block-fastest (5% faster so)
+  const int hfast = nb <= 65535;
+  hipLaunchKernelGGL(km_amax_kernel<D>, hfast ? dim3(H, nb, B) : dim3(nb, H, B), dim3(256), 0, st,
+                     v, S, H, ws.amax, hfast);
+  hipLaunchKernelGGL(km_codes_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax,
+                     ws.codes, ws.codes_t, 0);
   hipLaunchKernelGGL(km_init_kernel<D>, dim3(H, B), dim3(256), 0, st, ws.codes, S, H, kc, ws.cent);
   const int nasg = (S + kAsg - 1) / kAsg;
   for (int it = 0; it < iters; ++it) {

@@ -44,6 +44,20 @@ __device__ __forceinline__ float block_amax(float a, float* red4) {
   return a;
 }
 
+// Grid of one (block, head) per workgroup.  With token-major input (BSHD)
+// the head is the fastest index (hfast), so workgroups that run together
+// read neighbouring 256-byte pieces of the same token rows instead of rows
+// 128 tokens apart; with head-major input (BHSD) the block is.  gridDim.y
+// caps the slower index at 65535.
+struct BlockGrid {
+  dim3 grid;
+  int hfast;
+};
+inline BlockGrid block_grid(int layout, int nb, int H, int B) {
+  if (layout == VS_LAYOUT_BSHD && nb <= 65535) return {dim3(H, nb, B), 1};
+  return {dim3(nb, H, B), 0};
+}
+
 // Load TPT tokens x 8 channels of one block into float32 registers, with an
 // optional per-channel mean subtracted (one float32 subtraction).  Invalid
 // (padding) tokens are +0.
@@ -92,10 +106,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out, const float* __restrict__ k_mean,
-    float* __restrict__ q_mu, float c_log2) {
+    float* __restrict__ q_mu, float c_log2, int hfast) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   __shared__ float red4[4];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
+            b = blockIdx.z;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const float* mean8 = mean ? mean + bh * D + 8 * c : nullptr;
@@ -178,7 +193,7 @@ template <int D, bool OWN_MEAN>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
-    float* __restrict__ scale_out) {
+    float* __restrict__ scale_out, int hfast) {
   constexpr int CH = D / 8;              // 8-channel groups
   constexpr int QR = 256 / CH;           // quads in flight per pass
   constexpr int NQ = kBlock / 4 / QR;    // quads per thread
@@ -186,7 +201,8 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlock];
   __shared__ double part[OWN_MEAN ? QR : 1][OWN_MEAN ? D : 1];
   __shared__ float smean[OWN_MEAN ? D : 1];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
+            b = blockIdx.z;
   const int c = threadIdx.x % CH, a0 = threadIdx.x / CH;
   const size_t bh = static_cast<size_t>(b) * H + h;
   float mu[8];
@@ -319,29 +335,32 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
   const int nb = n_blocks(S);
   const float c_log2 = softmax_scale * 1.44269504088896341f;
   hipStream_t st = as_stream(stream);
-  const dim3 grid(nb, H, B), block(256);
+  const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
+  const dim3 block(256);
   if (D == 128) {
-    hipLaunchKernelGGL(quant_rows_kernel<128>, grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
-    hipLaunchKernelGGL(quant_rows_kernel<128>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       1.0f, k8, k_scale, nullptr, nullptr, c_log2);
+    hipLaunchKernelGGL(quant_rows_kernel<128>, gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
+                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
+                       gq.hfast);
+    hipLaunchKernelGGL(quant_rows_kernel<128>, gkv.grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
+                       1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast);
     if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-      hipLaunchKernelGGL((quant_vt_kernel<128, true>), grid, block, 0, st, v, kv_layout, S, H, nb,
-                         v_mean, vmean_mode, v8, v_scale);
+      hipLaunchKernelGGL((quant_vt_kernel<128, true>), gkv.grid, block, 0, st, v, kv_layout, S, H,
+                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
     else
-      hipLaunchKernelGGL((quant_vt_kernel<128, false>), grid, block, 0, st, v, kv_layout, S, H, nb,
-                         v_mean, vmean_mode, v8, v_scale);
+      hipLaunchKernelGGL((quant_vt_kernel<128, false>), gkv.grid, block, 0, st, v, kv_layout, S, H,
+                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
   } else {
-    hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2);
-    hipLaunchKernelGGL(quant_rows_kernel<64>, grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       1.0f, k8, k_scale, nullptr, nullptr, c_log2);
+    hipLaunchKernelGGL(quant_rows_kernel<64>, gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
+                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
+                       gq.hfast);
+    hipLaunchKernelGGL(quant_rows_kernel<64>, gkv.grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
+                       1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast);
     if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-      hipLaunchKernelGGL((quant_vt_kernel<64, true>), grid, block, 0, st, v, kv_layout, S, H, nb,
-                         v_mean, vmean_mode, v8, v_scale);
+      hipLaunchKernelGGL((quant_vt_kernel<64, true>), gkv.grid, block, 0, st, v, kv_layout, S, H,
+                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
     else
-      hipLaunchKernelGGL((quant_vt_kernel<64, false>), grid, block, 0, st, v, kv_layout, S, H, nb,
-                         v_mean, vmean_mode, v8, v_scale);
+      hipLaunchKernelGGL((quant_vt_kernel<64, false>), gkv.grid, block, 0, st, v, kv_layout, S, H,
+                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
   }
   return launch_status();
 }

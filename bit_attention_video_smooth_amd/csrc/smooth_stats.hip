@@ -24,13 +24,16 @@ template <int D>
 __global__ __launch_bounds__(256) void stats_block_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int layout,
     int S, int H, int nb, float* __restrict__ v_block_mean,
-    double* __restrict__ ws_k, double* __restrict__ ws_v) {
+    double* __restrict__ ws_k, double* __restrict__ ws_v, int hfast) {
   constexpr int CH = D / 8;           // 16-byte chunks per token row
   constexpr int ROWS = 256 / CH;      // token lanes per workgroup
   constexpr int TPT = kBlock / ROWS;  // tokens per thread
   __shared__ double red[ROWS][D];
 
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // token-major input: the head is the fastest grid index, so workgroups
+  // that run together read neighbouring pieces of the same token rows
+  const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
+            b = blockIdx.z;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
   double sk[8], sv[8];
 #pragma unroll
@@ -147,15 +150,16 @@ extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int 
   double* ws_k = static_cast<double*>(ws);
   double* ws_v = ws_k + static_cast<size_t>(B) * H * nb * D;
   hipStream_t st = as_stream(stream);
-  const dim3 g1(nb, H, B), g2(H, B);
+  const int hfast = layout == VS_LAYOUT_BSHD && nb <= 65535;
+  const dim3 g1 = hfast ? dim3(H, nb, B) : dim3(nb, H, B), g2(H, B);
   if (D == 128) {
     hipLaunchKernelGGL(stats_block_kernel<128>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
-                       v_block_mean, ws_k, ws_v);
+                       v_block_mean, ws_k, ws_v, hfast);
     hipLaunchKernelGGL(stats_seq_kernel<128>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
                        k_mean, v_seq_mean);
   } else {
     hipLaunchKernelGGL(stats_block_kernel<64>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
-                       v_block_mean, ws_k, ws_v);
+                       v_block_mean, ws_k, ws_v, hfast);
     hipLaunchKernelGGL(stats_seq_kernel<64>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
                        k_mean, v_seq_mean);
   }
