@@ -12,6 +12,7 @@ Modules
 e4m3       OCP FP8 E4M3 ("FN") codec from the format definition.
 smoothing  exact K/V statistics and the per-128-token-block quantizers.
 kmeans     integer Lloyd k-means on V, stable label sort, joint K/V gather.
+grouping   the static spatiotemporal-cube permutation of a video token grid.
 attention  FP64 dense attention, the tiled online-softmax recurrence with the
            rank-one V-mean restore, E4M3 / ExpCast-FP8 probability casts.
 matrix_core  E4M3 dot products in the arithmetic of the FP8 matrix core the

@@ -3,7 +3,8 @@
 Test infrastructure (see ``oracle/__init__``).
 
 1. optional V-Smooth grouping: integer k-means on V, stable label sort,
-   K and V permuted together (``kmeans``);
+   K and V permuted together (``kmeans``), or a given permutation (a static
+   cube grouping, ``grouping``, or one reused from an earlier call);
 2. exact statistics: mu_K over the sequence, mu_V per 128-token block (or
    over the sequence) (``smoothing``);
 3. per-block E4M3 quantization (power-of-two scales) of c Q, of K - mu_K
@@ -34,12 +35,14 @@ def default_scale(D: int) -> np.float32:
 
 
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
-                            smooth=True, vmean_mode="block", kmeans_kt=None,
+                            smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
                             expcast=False, pcast=None, fp32=True, scores="mfma"):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
-    evaluate (default all).  kmeans_kt: (k, iters) or None.  smooth: K
+    evaluate (default all).  kmeans_kt: (k, iters) or None.  perm: a given
+    permutation of the keys and values instead (a static cube grouping or a
+    permutation reused from an earlier call), or None.  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
     scores: "mfma" forms QK^T in the FP8 matrix core's arithmetic (the
     precision in which the kernel decides every P code), "exact" in float64.
@@ -58,9 +61,17 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     c = smoothing.score_constant(softmax_scale)
     out = {"rows": rows, "c": c}
 
+    if kmeans_kt is not None and perm is not None:
+        raise ValueError("k-means grouping and a given permutation are exclusive")
     if kmeans_kt is not None:
         labels, perm, kp, vp = kmeans.kmeans_permute_head(k, v, *kmeans_kt)
         out["labels"], out["perm"] = labels, perm
+    elif perm is not None:
+        perm = np.asarray(perm, dtype=np.int64)
+        if not np.array_equal(np.sort(perm), np.arange(S)):
+            raise ValueError("perm is not a permutation of the tokens")
+        kp, vp = k[perm], v[perm]
+        out["perm"] = perm
     else:
         kp, vp = k, v
     out["k_perm"], out["v_perm"] = kp, vp
