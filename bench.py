@@ -82,6 +82,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="live")
     ap.add_argument("--expcast", type=int, default=None, help="override the workload's ExpCast flag")
+    ap.add_argument("--gather", choices=["fused", "copy"], default="fused",
+                    help="k-means workloads: quantizers read K/V through the permutation "
+                         "(fused) or a gathered copy")
+    ap.add_argument("--reuse-perm", action="store_true",
+                    help="k-means workloads: timed steps keep the warm-up's permutation "
+                         "(grouping amortized away)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -106,7 +112,9 @@ def main():
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
     q, k, v = workloads.generate(w, device=dev)
-    plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast)
+    plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
+                   fused_gather=args.gather == "fused")
+    regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -124,7 +132,7 @@ def main():
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        plan.run(q, k, v)
+        plan.run(q, k, v, regroup=regroup)
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -159,6 +167,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}",
                    "kmeans": list(w.kmeans) if w.kmeans else None, "expcast": expcast,
+                   "gather": args.gather if w.kmeans else None,
+                   "grouping_per_step": bool(w.kmeans) and regroup,
                    "smoothing": "K seq-mean centring + V block-mean restore",
                    "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
                    "attn_ms": round(attn_ms, 4),

@@ -25,8 +25,11 @@ PROTOTYPES = {
     "vs_smooth_stats": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "vs_quantize_residual": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _I,
                                   _P, _P, _P, _P, _P, _P, _P, _P]),
+    "vs_quantize_residual_perm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I,
+                                       _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_fp8_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,
                              _P, _P, _P]),
+    "vs_cube_permutation": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "vs_kmeans_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _PZ]),
     "vs_kmeans_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
 }

@@ -19,7 +19,9 @@ from ._abi import (VS_EXPCAST, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
+           "vs_quantize_residual_perm",
            "vs_fp8_attn_fwd", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
+           "vs_cube_permutation",
            "vs_version", "Plan", "attention"]
 
 _VMEAN = {"none": VS_VMEAN_NONE, "block": VS_VMEAN_BLOCK, "seq": VS_VMEAN_SEQ}
@@ -73,6 +75,18 @@ def vs_quantize_residual(q, k, v, kv_layout, shape, softmax_scale, k_mean, v_mea
           "vs_quantize_residual")
 
 
+def vs_quantize_residual_perm(q, k, v, perm, shape, softmax_scale, k_mean, v_mean, vmean_mode,
+                              q8, q_scale, k8, k_scale, v8, v_scale, q_mu):
+    B, S, H, D = shape
+    dev = _dev(q, k, v)
+    check(load().vs_quantize_residual_perm(_p(q), _p(k), _p(v), _p(perm), B, S, H, D,
+                                           float(softmax_scale), _p(k_mean), _p(v_mean),
+                                           vmean_mode, _p(q8), _p(q_scale), _p(k8),
+                                           _p(k_scale), _p(v8), _p(v_scale), _p(q_mu),
+                                           _stream(dev)),
+          "vs_quantize_residual_perm")
+
+
 def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, shape,
                     flags, out, lse2):
     B, S, H, D = shape
@@ -80,6 +94,17 @@ def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q
     check(load().vs_fp8_attn_fwd(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v8), _p(v_scale),
                                  _p(v_mean), vmean_mode, _p(q_mu), B, S, H, D, int(flags),
                                  _p(out), _p(lse2), _stream(dev)), "vs_fp8_attn_fwd")
+
+
+def vs_cube_permutation(S, grid, cube):
+    """Host call: int32 CPU tensor [S], the static cube grouping of a
+    T x Hg x W token grid (include/vsmooth.h)."""
+    T, Hg, W = (int(a) for a in grid)
+    ct, ch, cw = (int(a) for a in cube)
+    perm = torch.empty(max(int(S), 0), dtype=torch.int32)
+    check(load().vs_cube_permutation(int(S), T, Hg, W, ct, ch, cw,
+                                     _p(perm) if perm.numel() else None), "vs_cube_permutation")
+    return perm
 
 
 def vs_kmeans_workspace_bytes(B, S, H, D, k_clusters):
@@ -103,11 +128,15 @@ class Plan:
 
     shape (B, S, H, D); smooth: K centring + V mean removal; vmean: "block"
     or "seq" (ignored when smooth is False); kmeans: (k, iters) or None;
-    expcast: ExpCast-FP8 P cast.
+    expcast: ExpCast-FP8 P cast; fused_gather (with kmeans): the quantizers
+    read K and V through the permutation (vs_quantize_residual_perm) instead
+    of a gathered copy (vs_kmeans_permute's k_perm / v_perm, then allocated);
+    cube: ((T, Hg, W), (ct, ch, cw)) groups the tokens by the static
+    spatiotemporal-cube permutation instead (formed once, here).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
-                 kmeans=None, expcast=False):
+                 kmeans=None, expcast=False, fused_gather=True, cube=None):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -131,15 +160,29 @@ class Plan:
             self.v_mean = e(B, H, nb, D) if self.vmean_mode == VS_VMEAN_BLOCK else e(B, H, D)
             self.stats_ws = e(vs_smooth_stats_workspace_bytes(B, S, H, D), dtype=u8)
         self.labels = self.perm = self.k_perm = self.v_perm = self.km_ws = None
+        self.cube = cube
+        self._grouped = False
+        if kmeans is not None and cube is not None:
+            raise ValueError("kmeans and cube grouping are exclusive")
+        if cube is not None:
+            grid, dims = cube
+            p = vs_cube_permutation(S, grid, dims).to(dev)
+            self.perm = p.expand(B, H, S).contiguous()
+            self._grouped = True
         if kmeans is not None:
             kc, _ = kmeans
             self.labels, self.perm = e(B, H, S, dtype=i32), e(B, H, S, dtype=i32)
-            self.k_perm = e(B, H, S, D, dtype=torch.bfloat16)
-            self.v_perm = e(B, H, S, D, dtype=torch.bfloat16)
+            if not fused_gather:
+                self.k_perm = e(B, H, S, D, dtype=torch.bfloat16)
+                self.v_perm = e(B, H, S, D, dtype=torch.bfloat16)
             self.km_ws = e(vs_kmeans_workspace_bytes(B, S, H, D, kc), dtype=u8)
 
-    def run(self, q, k, v):
-        """Launch the whole path on the current stream; returns (out, lse2)."""
+    def run(self, q, k, v, regroup=True):
+        """Launch the whole path on the current stream; returns (out, lse2).
+
+        regroup=False (k-means plans with the fused gather) keeps the
+        permutation of the previous call instead of clustering again (the
+        pages' amortized grouping reuses it across adjacent steps)."""
         shape = self.shape
         if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
             raise ValueError(f"expected q, k, v of shape {shape}")
@@ -148,11 +191,15 @@ class Plan:
                 raise ValueError("q, k, v must be contiguous bf16 tensors on the plan's device")
         layout = VS_LAYOUT_BSHD
         kk, vv = k, v
-        if self.kmeans is not None:
+        if not regroup and self.k_perm is not None:
+            raise ValueError("reusing a permutation needs the fused gather")
+        if self.kmeans is not None and (regroup or not self._grouped):
             kc, iters = self.kmeans
             vs_kmeans_permute(k, v, shape, kc, iters, self.labels, self.perm, self.k_perm,
                               self.v_perm, self.km_ws)
-            kk, vv, layout = self.k_perm, self.v_perm, VS_LAYOUT_BHSD
+            self._grouped = True
+            if self.k_perm is not None:
+                kk, vv, layout = self.k_perm, self.v_perm, VS_LAYOUT_BHSD
         qmode = self.vmean_mode
         if self.smooth:
             # block means come out of the V quantizer (VS_VMEAN_BLOCK_OUT), so
@@ -162,9 +209,16 @@ class Plan:
                             seq, self.stats_ws)
             if self.vmean_mode == VS_VMEAN_BLOCK:
                 qmode = VS_VMEAN_BLOCK_OUT
-        vs_quantize_residual(q, kk, vv, layout, shape, self.softmax_scale, self.k_mean,
-                             self.v_mean, qmode, self.q8, self.q_scale, self.k8,
-                             self.k_scale, self.v8, self.v_scale, self.q_mu)
+        if self.perm is not None and self.k_perm is None:
+            # K mean over the unpermuted K (permutation-invariant); the
+            # quantizers gather K and V rows through perm
+            vs_quantize_residual_perm(q, k, v, self.perm, shape, self.softmax_scale,
+                                      self.k_mean, self.v_mean, qmode, self.q8, self.q_scale,
+                                      self.k8, self.k_scale, self.v8, self.v_scale, self.q_mu)
+        else:
+            vs_quantize_residual(q, kk, vv, layout, shape, self.softmax_scale, self.k_mean,
+                                 self.v_mean, qmode, self.q8, self.q_scale, self.k8,
+                                 self.k_scale, self.v8, self.v_scale, self.q_mu)
         self.attn()
         return self.out, self.lse2
 

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvsmooth.so")
-SOURCES = ["status.hip", "smooth_stats.hip", "quantize.hip", "attn_fwd.hip", "kmeans.hip"]
+SOURCES = ["status.hip", "smooth_stats.hip", "quantize.hip", "attn_fwd.hip", "kmeans.hip",
+           "grouping.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

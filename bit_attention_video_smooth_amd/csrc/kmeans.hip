@@ -530,6 +530,7 @@ void run_kmeans(const uint16_t* k, const uint16_t* v, int B, int S, int H, int k
   hipLaunchKernelGGL(km_scan_kernel, dim3(H, B), dim3(256), 0, st, H, kc, nchunk, ws.chunk);
   hipLaunchKernelGGL(km_scatter_kernel, dim3(nchunk, H, B), dim3(256), 0, st, labels, S, H, kc,
                      nchunk, ws.chunk, perm);
+  if (!kp) return;
   constexpr int RPW = 256 / (D / 8);
   hipLaunchKernelGGL(km_gather_kernel<D>, dim3((S + RPW - 1) / RPW, H, B), dim3(256), 0, st, k, v, S,
                      H, perm, kp, vp);
@@ -557,10 +558,12 @@ extern "C" int vs_kmeans_permute(const uint16_t* k, const uint16_t* v, int B, in
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (k_clusters > 256) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
-  if (!k || !v || !labels || !perm || !k_perm || !v_perm) return VS_ERR_INVALID_ARG;
+  if (!k || !v || !labels || !perm) return VS_ERR_INVALID_ARG;
+  // both gather outputs or neither (then labels and perm only)
+  if ((k_perm == nullptr) != (v_perm == nullptr)) return VS_ERR_INVALID_ARG;
   const void* ptrs[] = {k, v, labels, perm, k_perm, v_perm};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return VS_ERR_UNSUPPORTED;
+    if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
   const size_t need = km_layout(B, S, H, D, k_clusters, nullptr, nullptr);
   if (!ws || ws_bytes < need) return VS_ERR_WORKSPACE;
   if (!aligned16(ws)) return VS_ERR_UNSUPPORTED;

@@ -19,6 +19,12 @@
 //            channel, tokens in the order the attention kernel's MFMA B/A
 //            operand layout consumes (transposed through LDS).
 // The Q pass also emits q_mu[s] = c * (q_s . mu_K) from the bf16 q.
+//
+// Gather fused in (vs_quantize_residual_perm): with a permutation, row i of
+// head h's K and V blocks is read from token perm[b, h, i] of the caller's
+// [B,S,H,D] tensors, so the permuted K and V are never written to HBM
+// (VC-Attention summary, Key Contribution 3: the grouping's gather is part of
+// the fused prologue).
 #include <float.h>
 
 #include "common.h"
@@ -58,13 +64,25 @@ inline BlockGrid block_grid(int layout, int nb, int H, int B) {
   return {dim3(nb, H, B), 0};
 }
 
+// Source token of block row `tok`: perm[b, h, tok] (BSHD input; entries
+// outside [0, S) are clamped, so a bad permutation cannot read out of
+// bounds), or tok itself without a permutation.
+template <bool PERM>
+__device__ __forceinline__ int src_token(const int32_t* __restrict__ perm, size_t bh, int S,
+                                         int tok) {
+  if (!PERM) return tok;
+  const int s = perm[bh * S + tok];
+  return s < 0 ? 0 : (s >= S ? S - 1 : s);
+}
+
 // Load TPT tokens x 8 channels of one block into float32 registers, with an
 // optional per-channel mean subtracted (one float32 subtraction).  Invalid
 // (padding) tokens are +0.
-template <int D>
+template <int D, bool PERM>
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int layout, int b,
                                            int h, int j, int S, int H,
                                            const float* __restrict__ mean8,
+                                           const int32_t* __restrict__ perm,
                                            float (&val)[kBlock / (256 / (D / 8))][8]) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
@@ -75,7 +93,8 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int l
   for (int i = 0; i < TPT; ++i) {
     const int tok = j * kBlock + r + ROWS * i;
     if (tok < S) {
-      const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, tok, h, S, H, D) + 8 * c);
+      const int src = src_token<PERM>(perm, static_cast<size_t>(b) * H + h, S, tok);
+      const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, src, h, S, H, D) + 8 * c);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -100,13 +119,13 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
 
 // Q (mean == nullptr, scaled by pre = c) or centred K (pre = 1): codes as
 // token rows.  With q_mu != nullptr also q_mu[s] = c * (q_s . k_mean) from
-// the bf16 q.
-template <int D>
+// the bf16 q.  PERM: rows gathered through perm (K only).
+template <int D, bool PERM>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out, const float* __restrict__ k_mean,
-    float* __restrict__ q_mu, float c_log2, int hfast) {
+    float* __restrict__ q_mu, float c_log2, int hfast, const int32_t* __restrict__ perm) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   __shared__ float red4[4];
   const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
@@ -116,7 +135,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const float* mean8 = mean ? mean + bh * D + 8 * c : nullptr;
 
   float val[TPT][8];
-  load_block<D>(x, layout, b, h, j, S, H, mean8, val);
+  load_block<D, PERM>(x, layout, b, h, j, S, H, mean8, perm, val);
 
   if (q_mu) {
     float km[8];
@@ -189,11 +208,11 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
 // per thread, then over the threads of a channel group in a fixed order, one
 // division, one rounding to float32, as vs_smooth_stats forms it -- written
 // to v_mean and subtracted.
-template <int D, bool OWN_MEAN>
+template <int D, bool OWN_MEAN, bool PERM>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
-    float* __restrict__ scale_out, int hfast) {
+    float* __restrict__ scale_out, int hfast, const int32_t* __restrict__ perm) {
   constexpr int CH = D / 8;              // 8-channel groups
   constexpr int QR = 256 / CH;           // quads in flight per pass
   constexpr int NQ = kBlock / 4 / QR;    // quads per thread
@@ -222,7 +241,8 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
     for (int q = 0; q < 4; ++q) {
       const int tok = j * kBlock + 4 * (a0 + QR * n) + q;
       if (tok < S) {
-        const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, tok, h, S, H, D) + 8 * c);
+        const int src = src_token<PERM>(perm, bh, S, tok);
+        const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, src, h, S, H, D) + 8 * c);
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -308,13 +328,34 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
 }  // namespace
 }  // namespace vs
 
-extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    int kv_layout, int B, int S, int H, int D,
-                                    float softmax_scale, const float* k_mean,
-                                    float* v_mean, int vmean_mode, uint8_t* q8,
-                                    float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8,
-                                    float* v_scale, float* q_mu, void* stream) {
-  using namespace vs;
+namespace vs {
+namespace {
+
+template <int D, bool PERM>
+void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, const uint16_t* q,
+                  const uint16_t* k, const uint16_t* v, int kv_layout, int S, int H, int nb,
+                  float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
+                  float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
+                  float* q_mu, const int32_t* perm) {
+  const dim3 block(256);
+  hipLaunchKernelGGL((quant_rows_kernel<D, false>), gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S,
+                     H, nb, nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
+                     gq.hfast, nullptr);
+  hipLaunchKernelGGL((quant_rows_kernel<D, PERM>), gkv.grid, block, 0, st, k, kv_layout, S, H, nb,
+                     k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
+  if (vmean_mode == VS_VMEAN_BLOCK_OUT)
+    hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM>), gkv.grid, block, 0, st, v, kv_layout, S,
+                       H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+  else
+    hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM>), gkv.grid, block, 0, st, v, kv_layout, S,
+                       H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+}
+
+int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, int kv_layout,
+                      const int32_t* perm, int B, int S, int H, int D, float softmax_scale,
+                      const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
+                      float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
+                      float* q_mu, void* stream) {
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
@@ -327,7 +368,7 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
   if (k_mean && !q_mu) return VS_ERR_INVALID_ARG;
   if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale)
     return VS_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, k_mean, v_mean, q8, q_scale, k8, k_scale, v8, v_scale, q_mu};
+  const void* ptrs[] = {q, k, v, k_mean, v_mean, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
@@ -336,31 +377,47 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
   const float c_log2 = softmax_scale * 1.44269504088896341f;
   hipStream_t st = as_stream(stream);
   const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
-  const dim3 block(256);
   if (D == 128) {
-    hipLaunchKernelGGL(quant_rows_kernel<128>, gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
-                       gq.hfast);
-    hipLaunchKernelGGL(quant_rows_kernel<128>, gkv.grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast);
-    if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-      hipLaunchKernelGGL((quant_vt_kernel<128, true>), gkv.grid, block, 0, st, v, kv_layout, S, H,
-                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
+    if (perm)
+      launch_quant<128, true>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
+                              vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm);
     else
-      hipLaunchKernelGGL((quant_vt_kernel<128, false>), gkv.grid, block, 0, st, v, kv_layout, S, H,
-                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
+      launch_quant<128, false>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
+                               vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, nullptr);
   } else {
-    hipLaunchKernelGGL(quant_rows_kernel<64>, gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S, H, nb,
-                       nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
-                       gq.hfast);
-    hipLaunchKernelGGL(quant_rows_kernel<64>, gkv.grid, block, 0, st, k, kv_layout, S, H, nb, k_mean,
-                       1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast);
-    if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-      hipLaunchKernelGGL((quant_vt_kernel<64, true>), gkv.grid, block, 0, st, v, kv_layout, S, H,
-                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
+    if (perm)
+      launch_quant<64, true>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
+                             vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm);
     else
-      hipLaunchKernelGGL((quant_vt_kernel<64, false>), gkv.grid, block, 0, st, v, kv_layout, S, H,
-                         nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast);
+      launch_quant<64, false>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
+                              vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, nullptr);
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace vs
+
+extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    int kv_layout, int B, int S, int H, int D,
+                                    float softmax_scale, const float* k_mean,
+                                    float* v_mean, int vmean_mode, uint8_t* q8,
+                                    float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8,
+                                    float* v_scale, float* q_mu, void* stream) {
+  return vs::quantize_residual(q, k, v, kv_layout, nullptr, B, S, H, D, softmax_scale, k_mean,
+                               v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
+                               stream);
+}
+
+extern "C" int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* perm, int B, int S, int H, int D,
+                                         float softmax_scale, const float* k_mean,
+                                         float* v_mean, int vmean_mode, uint8_t* q8,
+                                         float* q_scale, uint8_t* k8, float* k_scale,
+                                         uint8_t* v8, float* v_scale, float* q_mu,
+                                         void* stream) {
+  if (!perm && B > 0 && S > 0 && H > 0) return VS_ERR_INVALID_ARG;
+  return vs::quantize_residual(q, k, v, VS_LAYOUT_BSHD, perm, B, S, H, D, softmax_scale, k_mean,
+                               v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
+                               stream);
 }

@@ -143,6 +143,33 @@ int vs_quantize_residual(const uint16_t* q, const uint16_t* k,
                          void* stream);
 
 /*
+ * vs_quantize_residual_perm -- vs_quantize_residual with the grouping's
+ * gather fused in: the permuted K and V are never written.  Source:
+ * VC-Attention summary, Key Contribution 3 (gather, means and quantizers in
+ * one fused prologue) and Key Contribution 1 (keys and values permuted
+ * together by the sorted cluster labels).
+ *
+ *   q, k, v       bf16 [B,S,H,D] (BSHD), the caller's tensors.
+ *   perm          i32 [B,H,S] (vs_kmeans_permute's perm): position i of
+ *                 head h takes K and V of token perm[b,h,i].  Must be a
+ *                 permutation of 0..S-1 per head for the result to mean
+ *                 anything; entries outside [0, S) are clamped (never read
+ *                 out of bounds).  NULL is VS_ERR_INVALID_ARG.
+ *   all other arguments as vs_quantize_residual (v_mean holds the block
+ *   means of the permuted V; k_mean is permutation-invariant and may come
+ *   from vs_smooth_stats over the unpermuted K).
+ * Outputs are bit-identical to vs_quantize_residual on K[perm], V[perm] in
+ * VS_LAYOUT_BHSD.  Q is not permuted.
+ */
+int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* perm, int B,
+                              int S, int H, int D, float softmax_scale,
+                              const float* k_mean, float* v_mean,
+                              int vmean_mode, uint8_t* q8, float* q_scale,
+                              uint8_t* k8, float* k_scale, uint8_t* v8,
+                              float* v_scale, float* q_mu, void* stream);
+
+/*
  * vs_fp8_attn_fwd -- FP8 attention forward with the in-recurrence V-mean
  * restore.  Source: VC-Attention summary, Key Contributions 1-2 and
  * "Methodology in Plain English"; abstract (low-bit matrix cores for QK^T
@@ -192,7 +219,10 @@ int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
  *   labels        out i32 [B,H,S]: cluster of each token (last assignment).
  *   perm          out i32 [B,H,S]: perm[i] = source token of position i,
  *                 ascending label, original order within a label.
- *   k_perm, v_perm out bf16 [B,H,S,D] (BHSD): K[perm], V[perm] per head.
+ *   k_perm, v_perm out bf16 [B,H,S,D] (BHSD): K[perm], V[perm] per head;
+ *                 both NULL: no gather (labels and perm only, for
+ *                 vs_quantize_residual_perm, which reads K and V through
+ *                 perm itself).  Exactly one NULL is VS_ERR_INVALID_ARG.
  *   ws, ws_bytes  workspace of at least vs_kmeans_workspace_bytes().
  * Integer definition (bit-exact on any implementation): codes =
  * rint(V * 2^-e) with 2^e the smallest power of two such that
@@ -206,6 +236,29 @@ int vs_kmeans_permute(const uint16_t* k, const uint16_t* v, int B, int S,
                       int H, int D, int k_clusters, int iters, int32_t* labels,
                       int32_t* perm, uint16_t* k_perm, uint16_t* v_perm,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * vs_cube_permutation -- static spatiotemporal-cube grouping of a video
+ * token grid, a zero-cost alternative to k-means grouping.  Source:
+ * VC-Attention summary, Main Findings (block demeaning in sequence order,
+ * under a static spatiotemporal cube, after k-means grouping) and Key
+ * Contribution 3 (a grouping permutation reused across calls).
+ *
+ * HOST function: no GPU work, `perm` is host memory.
+ *   S             tokens; the grid T x Hg x W (raster order, token s at
+ *                 (t, y, x) with s = (t*Hg + y)*W + x) must hold them:
+ *                 T*Hg*W >= S; positions s >= S are empty.
+ *   ct, ch, cw    cube extent along t, y, x (>= 1).
+ *   perm          out i32 [S]: perm[i] = token at position i: cubes in
+ *                 raster order of the cube grid (the last cube along an
+ *                 axis may be shorter), tokens of a cube in raster order.
+ * To use it, broadcast it to [B,H,S] and pass it to
+ * vs_quantize_residual_perm (K and V permuted together, Q not).
+ * VS_ERR_INVALID_ARG for non-positive sizes, a grid smaller than S, or a
+ * NULL perm with S > 0.
+ */
+int vs_cube_permutation(int S, int T, int Hg, int W, int ct, int ch, int cw,
+                        int32_t* perm);
 
 #ifdef __cplusplus
 }

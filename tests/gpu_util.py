@@ -75,8 +75,9 @@ def plan_head(plan, b, h, rows):
     if plan.labels is not None:
         out["labels"] = g(plan.labels)
         out["perm"] = g(plan.perm)
-        out["k_perm"] = plan.k_perm[b, h].view(torch.int16).cpu().numpy()
-        out["v_perm"] = plan.v_perm[b, h].view(torch.int16).cpu().numpy()
+        if plan.k_perm is not None:
+            out["k_perm"] = plan.k_perm[b, h].view(torch.int16).cpu().numpy()
+            out["v_perm"] = plan.v_perm[b, h].view(torch.int16).cpu().numpy()
     assert out["O"].shape[0] == len(rows) and S >= len(rows)
     return out
 

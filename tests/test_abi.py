@@ -98,7 +98,15 @@ def test_quant_stats_kmeans_argument_errors(lib):
     assert s(fake, None, 1, 300, 2, 128, 0, fake, None, fake, fake, 1 << 30, None) == 1
     assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, fake, 16, None) == 3
     assert s(fake, fake, 1, 300, 2, 128, 0, fake, None, None, None, 1 << 30, None) == 3
+    qp = lib.vs_quantize_residual_perm
+    assert qp(fake, fake, fake, None, 1, 300, 2, 128, 0.1, None, None, 0,
+              fake, fake, fake, fake, fake, fake, None, None) == 1   # no permutation
+    assert qp(fake, fake, fake, fake, 1, 300, 2, 32, 0.1, None, None, 0,
+              fake, fake, fake, fake, fake, fake, None, None) == 2
+    assert qp(fake, fake, fake, None, 1, 0, 2, 128, 0.1, None, None, 0,
+              fake, fake, fake, fake, fake, fake, None, None) == 0   # empty problem
     k = lib.vs_kmeans_permute
+    assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, None, fake, 1 << 30, None) == 1
     assert k(fake, fake, 1, 300, 2, 128, 16, 0, fake, fake, fake, fake, fake, 1 << 30, None) == 1
     assert k(fake, fake, 1, 300, 2, 128, 300, 2, fake, fake, fake, fake, fake, 1 << 30, None) == 2
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, fake, fake, 64, None) == 3
@@ -111,3 +119,27 @@ def test_header_constants_match_the_binding():
                  "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
+
+
+@pytest.mark.parametrize("S,grid,cube", [(16, (2, 2, 4), (1, 2, 2)), (8, (1, 3, 3), (1, 2, 2)),
+                                         (32626, (20, 48, 34), (2, 8, 8)),
+                                         (115328, (71, 48, 34), (1, 8, 16)),
+                                         (600, (5, 12, 10), (2, 4, 4)), (1, (1, 1, 1), (3, 3, 3))])
+def test_cube_permutation_host_call_equals_the_oracle(lib, S, grid, cube):
+    """vs_cube_permutation is a host function: checked here, without a GPU,
+    against the oracle's sort-based definition."""
+    import numpy as np
+    from oracle import grouping
+    buf = (ctypes.c_int32 * S)()
+    assert lib.vs_cube_permutation(S, *grid, *cube, buf) == 0
+    got = np.frombuffer(buf, dtype=np.int32).astype(np.int64)
+    np.testing.assert_array_equal(got, grouping.cube_permutation(S, grid, cube))
+
+
+def test_cube_permutation_argument_errors(lib):
+    buf = (ctypes.c_int32 * 64)()
+    assert lib.vs_cube_permutation(64, 2, 3, 4, 1, 1, 1, buf) == 1      # grid 24 < 64
+    assert lib.vs_cube_permutation(8, 2, 2, 2, 0, 1, 1, buf) == 1
+    assert lib.vs_cube_permutation(8, 2, 2, 2, 1, 1, 1, None) == 1
+    assert lib.vs_cube_permutation(-1, 2, 2, 2, 1, 1, 1, buf) == 1
+    assert lib.vs_cube_permutation(0, 2, 2, 2, 1, 1, 1, None) == 0

@@ -69,23 +69,44 @@ def test_ragged_and_tiny_shapes(S, D):
                 check_attn(got["O"], got["lse2"], ref, label=f"S{S} D{D} b{b} h{h} ec{expcast}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("D,S,kc,iters", [(128, 3000, 16, 4), (64, 2500, 32, 3),
                                           (128, 700, 200, 2)])
-def test_kmeans_permute_and_grouped_attention(D, S, kc, iters):
+def test_kmeans_permute_and_grouped_attention(D, S, kc, iters, fused):
+    """Grouping, then the quantizers on the gathered copy (fused=False) or
+    reading K and V through the permutation (vs_quantize_residual_perm)."""
     w = workloads.Workload("g", 1, S, 3, D, 7 + kc, "mixture", kmeans=(kc, iters),
                            extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
     q, k, v = workloads.generate(w)
-    plan = run_plan(q, k, v, kmeans=(kc, iters))
+    plan = run_plan(q, k, v, kmeans=(kc, iters), fused_gather=fused)
+    assert (plan.k_perm is None) == fused
     rows = _rows(S, 128)
     for h in range(3):
         ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=(kc, iters))
         got = plan_head(plan, 0, h, rows)
         check_intermediates(got, ref, S, label=f"kmeans h{h}")
-        kb = k[0, :, h, :].view(torch.int16).numpy()
-        vb = v[0, :, h, :].view(torch.int16).numpy()
-        np.testing.assert_array_equal(got["k_perm"], kb[ref["perm"]])
-        np.testing.assert_array_equal(got["v_perm"], vb[ref["perm"]])
-        check_attn(got["O"], got["lse2"], ref, label=f"kmeans D{D} h{h}")
+        if not fused:
+            kb = k[0, :, h, :].view(torch.int16).numpy()
+            vb = v[0, :, h, :].view(torch.int16).numpy()
+            np.testing.assert_array_equal(got["k_perm"], kb[ref["perm"]])
+            np.testing.assert_array_equal(got["v_perm"], vb[ref["perm"]])
+        check_attn(got["O"], got["lse2"], ref, label=f"kmeans D{D} h{h} fused{int(fused)}")
+
+
+@pytest.mark.parametrize("S,H,D,vmean", [(8192, 8, 128, "block"), (1000, 3, 64, "block"),
+                                         (2049, 2, 128, "seq")])
+def test_fused_gather_equals_gathered_copy(S, H, D, vmean):
+    """Every output of the fused-gather path equals, bit for bit, that of the
+    path through vs_kmeans_permute's gathered K', V' (all heads)."""
+    w = workloads.Workload("g", 1, S, H, D, 11, "mixture", kmeans=(16, 3),
+                           extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    q, k, v = workloads.generate(w)
+    a = run_plan(q, k, v, kmeans=(16, 3), vmean=vmean, fused_gather=False)
+    b = run_plan(q, k, v, kmeans=(16, 3), vmean=vmean, fused_gather=True)
+    for name in ("labels", "perm", "q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "k_mean",
+                 "v_mean", "q_mu", "out", "lse2"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name
 
 
 def test_e4m3_conversion_at_rounding_boundaries():
@@ -260,3 +281,62 @@ def test_block_means_from_the_quantizer_equal_the_statistics_pass(S, D, layout):
         for h in range(H):
             want = smoothing.v_block_means(v[b_, :, h, :].float().numpy())
             np.testing.assert_array_equal(fus["vm"][b_, h].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("S,grid,cube,D", [(1000, (4, 16, 16), (2, 8, 8), 128),
+                                           (700, (3, 16, 16), (1, 8, 16), 64)])
+def test_cube_grouping(S, grid, cube, D):
+    """Static spatiotemporal-cube grouping: the permutation the plan forms
+    (host call) equals the oracle's, and codes, means and attention match the
+    oracle run with that permutation."""
+    from oracle import grouping
+    if D == 128:   # the 3D RoPE recipe splits 128 channels 44/42/42
+        w = workloads.Workload("c", 1, S, 2, D, 23, "rope_drift",
+                               extra=dict(grid=grid, out_frac=0.005, out_mult=25.0))
+    else:
+        w = workloads.Workload("c", 1, S, 2, D, 23, "offsets",
+                               extra=dict(k_off=3.0, k_off_shared=True, v_off=2.0,
+                                          out_frac=0.005, out_mult=20.0))
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, cube=(grid, cube))
+    perm = grouping.cube_permutation(S, grid, cube)
+    np.testing.assert_array_equal(plan.perm[0, 1].cpu().numpy(), perm)
+    rows = np.arange(S)
+    for h in range(2):
+        ref = oracle_head(q, k, v, 0, h, rows, perm=perm)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, S, label=f"cube h{h}")
+        check_attn(got["O"], got["lse2"], ref, label=f"cube D{D} h{h}")
+
+
+def test_permutation_reused_across_calls():
+    """run(regroup=False) keeps the last call's k-means permutation: on new
+    inputs the result equals the oracle with that permutation given, and
+    differs from a fresh grouping of the new inputs."""
+    S, D, kc, iters = 1500, 128, 16, 3
+    w1 = workloads.Workload("g", 1, S, 2, D, 31, "mixture", kmeans=(kc, iters),
+                            extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    w2 = workloads.Workload("g", 1, S, 2, D, 32, "mixture", kmeans=(kc, iters),
+                            extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    q1, k1, v1 = workloads.generate(w1)
+    q2, k2, v2 = workloads.generate(w2)
+    import bit_attention_video_smooth_amd as vs
+    d = dev()
+    plan = vs.Plan((1, S, 2, D), d, kmeans=(kc, iters))
+    with pytest.raises(ValueError):
+        vs.Plan((1, S, 2, D), d, kmeans=(kc, iters), fused_gather=False).run(
+            q1.to(d), k1.to(d), v1.to(d), regroup=False)
+    plan.run(q1.to(d), k1.to(d), v1.to(d))
+    p1 = plan.perm.clone()
+    plan.run(q2.to(d), k2.to(d), v2.to(d), regroup=False)
+    torch.cuda.synchronize(d)
+    assert torch.equal(plan.perm, p1)
+    rows = _rows(S, 200)
+    for h in range(2):
+        perm = p1[0, h].cpu().numpy().astype(np.int64)
+        ref = oracle_head(q2, k2, v2, 0, h, rows, perm=perm)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, S, label=f"reuse h{h}")
+        check_attn(got["O"], got["lse2"], ref, label=f"reuse h{h}")
+        fresh = oracle_head(q2, k2, v2, 0, h, rows[:1], kmeans_kt=(kc, iters))
+        assert not np.array_equal(fresh["perm"], perm)
