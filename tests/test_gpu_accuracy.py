@@ -3,9 +3,11 @@ the unsmoothed FP8 path, at the five workloads' full sizes (TeleFuser PR
 #40, "Smooth Attention Kernel Accuracy": smoothing lowers the attention
 output error).  Reported per workload and head: relative L2, MSE, cosine
 and SQNR of O with smoothing on and off; for the ExpCast workload also the
-smoothed path with ExpCast off; for the grouped workloads the share of V
-energy the block means remove, in sequence order and in k-means order
-(VC-Attention summary, Main Findings), from the oracle's own grouping.
+smoothed path with ExpCast off; for the video-grid workloads also the
+smoothed path grouped by the static 2x8x8 spatiotemporal cube instead; the
+share of V energy the block means remove in sequence order, k-means order
+and cube order (VC-Attention summary, Main Findings), from the oracle's own
+grouping.
 Asserted: both errors are finite and small, for the workloads whose K
 carries a large per-channel offset (the case K centring targets) smoothing
 lowers the error, and grouping raises the removed energy."""
@@ -14,21 +16,22 @@ import pytest
 import torch
 
 import workloads
-from oracle import attention, kmeans, pipeline
+from oracle import attention, grouping, kmeans, pipeline
 from gpu_util import dev
 
 pytestmark = pytest.mark.gpu
 
 # workloads whose K has a large channel offset (N(0,3) / N(0,4) per channel)
 OFFSET_K = {"tiny", "mid"}
+CUBE = (2, 8, 8)
 
 
-def _outputs(w, q, k, v, smooth, expcast=None):
+def _outputs(w, q, k, v, smooth, expcast=None, cube=None):
     import bit_attention_video_smooth_amd as vs
     d = dev()
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, smooth=smooth,
-                   kmeans=w.kmeans if smooth else None,
-                   expcast=w.expcast if expcast is None else expcast)
+                   kmeans=w.kmeans if smooth and cube is None else None,
+                   expcast=w.expcast if expcast is None else expcast, cube=cube)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     return plan.out
@@ -44,10 +47,13 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
     cases = {"smoothed": _outputs(w, q, k, v, True), "unsmoothed": _outputs(w, q, k, v, False)}
     if w.expcast:
         cases["smoothed, ExpCast off"] = _outputs(w, q, k, v, True, expcast=False)
+    grid = w.extra.get("grid")
+    if grid is not None:
+        cases["smoothed, cube grouping"] = _outputs(w, q, k, v, True, cube=(grid, CUBE))
     rows = pipeline.sample_rows(w.S, 32)
     scale = pipeline.default_scale(w.D)
     errs = {c: [] for c in cases}
-    energy = {"sequence": [], "k-means": []}
+    energy = {"sequence": [], "k-means": [], "cube": []}
     for h in sorted({0, w.H // 2, w.H - 1}):
         qh, kh, vh = workloads.head_slices(q, k, v, 0, h)
         ref, _ = attention.dense_attention(qh[rows], kh, vh, scale)
@@ -58,10 +64,14 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
             errs[c].append(e)
             print(f"[accuracy] {name} h{h} {c}: rel_l2 {e['rel_l2']:.4e} mse {e['mse']:.4e} "
                   f"cos {e['cos']:.8f} sqnr {e['sqnr_db']:.2f} dB", flush=True)
+        if w.kmeans is not None or grid is not None:
+            energy["sequence"].append(kmeans.block_energy_removed(vh))
         if w.kmeans is not None:
             _, _, _, vp = kmeans.kmeans_permute_head(kh, vh, *w.kmeans)
-            energy["sequence"].append(kmeans.block_energy_removed(vh))
             energy["k-means"].append(kmeans.block_energy_removed(vp))
+        if grid is not None:
+            vc = vh[grouping.cube_permutation(w.S, grid, CUBE)]
+            energy["cube"].append(kmeans.block_energy_removed(vc))
     mean = {c: {m: float(np.mean([e[m] for e in errs[c]])) for m in ("rel_l2", "mse", "cos", "sqnr_db")}
             for c in cases}
     for c, m in mean.items():
@@ -72,8 +82,13 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
     assert sm < 0.1 and un < 0.5
     if name in OFFSET_K:
         assert sm < un
-    if w.kmeans is not None:
-        es, ek = float(np.mean(energy["sequence"])), float(np.mean(energy["k-means"]))
-        print(f"[accuracy] {name} V energy removed by the block means: sequence order {es:.4f}, "
-              f"k-means order {ek:.4f}", flush=True)
-        assert ek > es
+    if energy["sequence"]:
+        es = float(np.mean(energy["sequence"]))
+        line = f"[accuracy] {name} V energy removed by the block means: sequence order {es:.4f}"
+        if energy["k-means"]:
+            line += f", k-means order {float(np.mean(energy['k-means'])):.4f}"
+        if energy["cube"]:
+            line += f", cube {CUBE} order {float(np.mean(energy['cube'])):.4f}"
+        print(line, flush=True)
+        if w.kmeans is not None:
+            assert float(np.mean(energy["k-means"])) > es
