@@ -9,6 +9,7 @@ Test infrastructure (see ``oracle/__init__``).
    over the sequence) (``smoothing``);
 3. per-block E4M3 quantization (power-of-two scales) of c Q, of K - mu_K
    and of the V residual, and qmu = c q.mu_K from the bf16 q (``smoothing``);
+   optionally Q and the centred K rotated by a Hadamard matrix first;
 4. the tiled recurrence with the rank-one mean restore and the chosen P cast
    (``attention``).
 
@@ -36,13 +37,16 @@ def default_scale(D: int) -> np.float32:
 
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
-                            expcast=False, pcast=None, fp32=True, scores="mfma"):
+                            qk_hadamard=False, expcast=False, pcast=None, fp32=True,
+                            scores="mfma"):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
     evaluate (default all).  kmeans_kt: (k, iters) or None.  perm: a given
     permutation of the keys and values instead (a static cube grouping or a
-    permutation reused from an earlier call), or None.  smooth: K
+    permutation reused from an earlier call), or None.  qk_hadamard: Q and
+    the centred K rotated by H_D before quantization (smoothing docstring).
+    smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
     scores: "mfma" forms QK^T in the FP8 matrix core's arithmetic (the
     precision in which the kernel decides every P code), "exact" in float64.
@@ -94,7 +98,12 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     out.update(k_mean=k_mean, v_mean=v_mean, vmean_mode=vmean_mode,
                v_block_means=smoothing.v_block_means(vp) if smooth else None)
 
-    q_codes, q_scale = smoothing.quantize_blocks(smoothing.prescale_queries(q, c))
+    if qk_hadamard:
+        qpre = smoothing.hadamard_prescale_queries(q, c)
+        kc = smoothing.hadamard_rows_f32(kc)
+    else:
+        qpre = smoothing.prescale_queries(q, c)
+    q_codes, q_scale = smoothing.quantize_blocks(qpre)
     k_codes, k_scale = smoothing.quantize_blocks(kc)
     v_codes, v_scale = smoothing.quantize_blocks(vr)
     out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
