@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--reuse-perm", action="store_true",
                     help="k-means workloads: timed steps keep the warm-up's permutation "
                          "(grouping amortized away)")
+    ap.add_argument("--qk-hadamard", action="store_true",
+                    help="rotate Q and the centred K by the Hadamard matrix in the quantizers")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -113,7 +115,7 @@ def main():
     print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
     q, k, v = workloads.generate(w, device=dev)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
-                   fused_gather=args.gather == "fused")
+                   fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard)
     regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
@@ -169,6 +171,7 @@ def main():
                    "kmeans": list(w.kmeans) if w.kmeans else None, "expcast": expcast,
                    "gather": args.gather if w.kmeans else None,
                    "grouping_per_step": bool(w.kmeans) and regroup,
+                   "qk_hadamard": bool(args.qk_hadamard),
                    "smoothing": "K seq-mean centring + V block-mean restore",
                    "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
                    "attn_ms": round(attn_ms, 4),

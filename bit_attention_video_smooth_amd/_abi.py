@@ -9,6 +9,7 @@ VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = ra
 VS_LAYOUT_BSHD, VS_LAYOUT_BHSD = 0, 1
 VS_VMEAN_NONE, VS_VMEAN_BLOCK, VS_VMEAN_SEQ, VS_VMEAN_BLOCK_OUT = 0, 1, 2, 3
 VS_EXPCAST = 1
+VS_QK_HADAMARD = 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -27,6 +28,8 @@ PROTOTYPES = {
                                   _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_quantize_residual_perm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I,
                                        _P, _P, _P, _P, _P, _P, _P, _P]),
+    "vs_quantize_residual_ex": (_I, [_P, _P, _P, _I, _P, _U, _I, _I, _I, _I, _F, _P, _P, _I,
+                                     _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_fp8_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,
                              _P, _P, _P]),
     "vs_cube_permutation": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),

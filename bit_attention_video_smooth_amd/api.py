@@ -15,11 +15,11 @@ import math
 import torch
 
 from . import _abi
-from ._abi import (VS_EXPCAST, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+from ._abi import (VS_EXPCAST, VS_QK_HADAMARD, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
-           "vs_quantize_residual_perm",
+           "vs_quantize_residual_perm", "vs_quantize_residual_ex",
            "vs_fp8_attn_fwd", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
            "vs_cube_permutation",
            "vs_version", "Plan", "attention"]
@@ -87,6 +87,18 @@ def vs_quantize_residual_perm(q, k, v, perm, shape, softmax_scale, k_mean, v_mea
           "vs_quantize_residual_perm")
 
 
+def vs_quantize_residual_ex(q, k, v, kv_layout, perm, flags, shape, softmax_scale, k_mean, v_mean,
+                            vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu):
+    B, S, H, D = shape
+    dev = _dev(q, k, v)
+    check(load().vs_quantize_residual_ex(_p(q), _p(k), _p(v), kv_layout, _p(perm), int(flags),
+                                         B, S, H, D, float(softmax_scale), _p(k_mean),
+                                         _p(v_mean), vmean_mode, _p(q8), _p(q_scale), _p(k8),
+                                         _p(k_scale), _p(v8), _p(v_scale), _p(q_mu),
+                                         _stream(dev)),
+          "vs_quantize_residual_ex")
+
+
 def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, shape,
                     flags, out, lse2):
     B, S, H, D = shape
@@ -132,11 +144,13 @@ class Plan:
     read K and V through the permutation (vs_quantize_residual_perm) instead
     of a gathered copy (vs_kmeans_permute's k_perm / v_perm, then allocated);
     cube: ((T, Hg, W), (ct, ch, cw)) groups the tokens by the static
-    spatiotemporal-cube permutation instead (formed once, here).
+    spatiotemporal-cube permutation instead (formed once, here);
+    qk_hadamard: Q and the centred K rotated by the Hadamard matrix before
+    quantization (VS_QK_HADAMARD).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
-                 kmeans=None, expcast=False, fused_gather=True, cube=None):
+                 kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -145,6 +159,7 @@ class Plan:
         self.vmean_mode = _VMEAN[vmean] if smooth else VS_VMEAN_NONE
         self.kmeans = kmeans
         self.flags = VS_EXPCAST if expcast else 0
+        self.quant_flags = VS_QK_HADAMARD if qk_hadamard else 0
         nb = (S + 127) // 128
         dev = self.device
         f32, u8, i32 = torch.float32, torch.uint8, torch.int32
@@ -209,16 +224,14 @@ class Plan:
                             seq, self.stats_ws)
             if self.vmean_mode == VS_VMEAN_BLOCK:
                 qmode = VS_VMEAN_BLOCK_OUT
-        if self.perm is not None and self.k_perm is None:
-            # K mean over the unpermuted K (permutation-invariant); the
-            # quantizers gather K and V rows through perm
-            vs_quantize_residual_perm(q, k, v, self.perm, shape, self.softmax_scale,
-                                      self.k_mean, self.v_mean, qmode, self.q8, self.q_scale,
-                                      self.k8, self.k_scale, self.v8, self.v_scale, self.q_mu)
-        else:
-            vs_quantize_residual(q, kk, vv, layout, shape, self.softmax_scale, self.k_mean,
-                                 self.v_mean, qmode, self.q8, self.q_scale, self.k8,
-                                 self.k_scale, self.v8, self.v_scale, self.q_mu)
+        # with a permutation and no gathered copy the quantizers read K and V
+        # rows through it (the K mean, permutation-invariant, came from the
+        # unpermuted K)
+        perm = self.perm if (self.perm is not None and self.k_perm is None) else None
+        vs_quantize_residual_ex(q, kk, vv, layout, perm, self.quant_flags, shape,
+                                self.softmax_scale, self.k_mean, self.v_mean, qmode, self.q8,
+                                self.q_scale, self.k8, self.k_scale, self.v8, self.v_scale,
+                                self.q_mu)
         self.attn()
         return self.out, self.lse2
 

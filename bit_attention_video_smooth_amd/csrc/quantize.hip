@@ -89,11 +89,19 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int l
   float mu[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mu[e] = mean8 ? mean8[e] : 0.0f;
+  // permuted rows: all source indices first, so their loads overlap
+  int srcs[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int tok = j * kBlock + r + ROWS * i;
+    srcs[i] = PERM ? src_token<PERM>(perm, static_cast<size_t>(b) * H + h, S, tok < S ? tok : S - 1)
+                   : tok;
+  }
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int tok = j * kBlock + r + ROWS * i;
     if (tok < S) {
-      const int src = src_token<PERM>(perm, static_cast<size_t>(b) * H + h, S, tok);
+      const int src = srcs[i];
       const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, src, h, S, H, D) + 8 * c);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -108,6 +116,59 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int l
   }
 }
 
+// x of lane (lane ^ J), J in {1, 2, 4, 8}: DPP quad permutations for 1 and
+// 2, the swizzle unit's bit-mask mode (xor within 32 lanes) for 4 and 8 --
+// no LDS address round trip.
+__device__ __forceinline__ float lane_xor(float x, int j) {
+  const int v = __float_as_int(x);
+  int r;
+  switch (j) {
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); break;  // quad [1,0,3,2]
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); break;  // quad [2,3,0,1]
+    case 4: r = __builtin_amdgcn_ds_swizzle(v, 0x101F); break;              // and 0x1F, xor 4
+    default: r = __builtin_amdgcn_ds_swizzle(v, 0x201F); break;             // and 0x1F, xor 8
+  }
+  return __int_as_float(r);
+}
+
+// Rows of a block times the Sylvester Hadamard matrix H_D (entries +-1),
+// in float32: the butterfly (a, b) -> (a + b, a - b) over channel bit 0,
+// then bit 1, and so on -- channel bits 0-2 inside a thread's 8 channels,
+// the higher bits across the CH lanes of a token row (lane bit j holds
+// channel bit 3 + j), where the lane with the bit set keeps its partner's
+// value minus its own.  Each sum and difference is rounded once, in this
+// order (it decides the codes).  (VC-Attention summary, Key Contribution 3:
+// the QK Hadamard rotation belongs to the fused quantizer prologue.)
+template <int D>
+__device__ __forceinline__ void hadamard_rows(float (&val)[kBlock / (256 / (D / 8))][8]) {
+  constexpr int CH = D / 8, TPT = kBlock / (256 / CH);
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & h)) {
+          const float a = val[i][e], b = val[i][e + h];
+          val[i][e] = a + b;
+          val[i][e + h] = a - b;
+        }
+  }
+  const int c = threadIdx.x % CH;
+#pragma unroll
+  for (int j = 1; j < CH; j <<= 1) {
+    const bool hi = (c & j) != 0;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = val[i][e];
+        const float y = lane_xor(x, j);
+        val[i][e] = hi ? y - x : x + y;
+      }
+  }
+}
+
 // Smallest e >= -126 with amax <= 448 * 2^e (0 when amax == 0).
 __device__ __forceinline__ int pow2_exponent(float amax) {
   if (!(amax > 0.0f)) return 0;
@@ -119,8 +180,10 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
 
 // Q (mean == nullptr, scaled by pre = c) or centred K (pre = 1): codes as
 // token rows.  With q_mu != nullptr also q_mu[s] = c * (q_s . k_mean) from
-// the bf16 q.  PERM: rows gathered through perm (K only).
-template <int D, bool PERM>
+// the bf16 q.  PERM: rows gathered through perm (K only).  HAD: rows
+// rotated by H_D after the centring and before the scaling by pre (the
+// caller folds Q's 1/D into pre).
+template <int D, bool PERM, bool HAD>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
@@ -153,6 +216,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     }
   }
 
+  if (HAD) hadamard_rows<D>(val);
   if (pre != 1.0f) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i)
@@ -234,6 +298,15 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
   }
 
   // residuals in float32; padding tokens are +0
+  // permuted rows: all source indices first, so their loads overlap
+  int srcs[NQ][4];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tok = j * kBlock + 4 * (a0 + QR * n) + q;
+      srcs[n][q] = PERM ? src_token<PERM>(perm, bh, S, tok < S ? tok : S - 1) : tok;
+    }
   float val[NQ][4][8];
 #pragma unroll
   for (int n = 0; n < NQ; ++n)
@@ -241,7 +314,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
     for (int q = 0; q < 4; ++q) {
       const int tok = j * kBlock + 4 * (a0 + QR * n) + q;
       if (tok < S) {
-        const int src = src_token<PERM>(perm, bh, S, tok);
+        const int src = srcs[n][q];
         const uint4 w = *reinterpret_cast<const uint4*>(x + token_offset(layout, b, src, h, S, H, D) + 8 * c);
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -331,18 +404,20 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
 namespace vs {
 namespace {
 
-template <int D, bool PERM>
+template <int D, bool PERM, bool HAD>
 void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, const uint16_t* q,
                   const uint16_t* k, const uint16_t* v, int kv_layout, int S, int H, int nb,
                   float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
                   float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
                   float* q_mu, const int32_t* perm) {
   const dim3 block(256);
-  hipLaunchKernelGGL((quant_rows_kernel<D, false>), gq.grid, block, 0, st, q, VS_LAYOUT_BSHD, S,
-                     H, nb, nullptr, c_log2, q8, q_scale, k_mean, k_mean ? q_mu : nullptr, c_log2,
-                     gq.hfast, nullptr);
-  hipLaunchKernelGGL((quant_rows_kernel<D, PERM>), gkv.grid, block, 0, st, k, kv_layout, S, H, nb,
-                     k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
+  // with the rotation Q carries its 1/D (a power of two: exact)
+  const float q_pre = HAD ? c_log2 * (1.0f / D) : c_log2;
+  hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD>), gq.grid, block, 0, st, q,
+                     VS_LAYOUT_BSHD, S, H, nb, nullptr, q_pre, q8, q_scale, k_mean,
+                     k_mean ? q_mu : nullptr, c_log2, gq.hfast, nullptr);
+  hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD>), gkv.grid, block, 0, st, k, kv_layout, S,
+                     H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
   if (vmean_mode == VS_VMEAN_BLOCK_OUT)
     hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM>), gkv.grid, block, 0, st, v, kv_layout, S,
                        H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
@@ -352,12 +427,15 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
 }
 
 int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, int kv_layout,
-                      const int32_t* perm, int B, int S, int H, int D, float softmax_scale,
+                      const int32_t* perm, unsigned flags, int B, int S, int H, int D,
+                      float softmax_scale,
                       const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
                       float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
                       float* q_mu, void* stream) {
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
+  if (perm && kv_layout != VS_LAYOUT_BSHD) return VS_ERR_INVALID_ARG;
+  if (flags & ~VS_QK_HADAMARD) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
       vmean_mode != VS_VMEAN_BLOCK_OUT)
     return VS_ERR_INVALID_ARG;
@@ -377,21 +455,17 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   const float c_log2 = softmax_scale * 1.44269504088896341f;
   hipStream_t st = as_stream(stream);
   const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
+#define VS_QUANT_ARGS gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean, \
+    vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm
+  const bool had = (flags & VS_QK_HADAMARD) != 0;
   if (D == 128) {
-    if (perm)
-      launch_quant<128, true>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
-                              vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm);
-    else
-      launch_quant<128, false>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
-                               vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, nullptr);
+    if (perm) had ? launch_quant<128, true, true>(VS_QUANT_ARGS) : launch_quant<128, true, false>(VS_QUANT_ARGS);
+    else had ? launch_quant<128, false, true>(VS_QUANT_ARGS) : launch_quant<128, false, false>(VS_QUANT_ARGS);
   } else {
-    if (perm)
-      launch_quant<64, true>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
-                             vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm);
-    else
-      launch_quant<64, false>(gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean,
-                              vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, nullptr);
+    if (perm) had ? launch_quant<64, true, true>(VS_QUANT_ARGS) : launch_quant<64, true, false>(VS_QUANT_ARGS);
+    else had ? launch_quant<64, false, true>(VS_QUANT_ARGS) : launch_quant<64, false, false>(VS_QUANT_ARGS);
   }
+#undef VS_QUANT_ARGS
   return launch_status();
 }
 
@@ -404,7 +478,7 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
                                     float* v_mean, int vmean_mode, uint8_t* q8,
                                     float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8,
                                     float* v_scale, float* q_mu, void* stream) {
-  return vs::quantize_residual(q, k, v, kv_layout, nullptr, B, S, H, D, softmax_scale, k_mean,
+  return vs::quantize_residual(q, k, v, kv_layout, nullptr, 0u, B, S, H, D, softmax_scale, k_mean,
                                v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
                                stream);
 }
@@ -417,7 +491,18 @@ extern "C" int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k, c
                                          uint8_t* v8, float* v_scale, float* q_mu,
                                          void* stream) {
   if (!perm && B > 0 && S > 0 && H > 0) return VS_ERR_INVALID_ARG;
-  return vs::quantize_residual(q, k, v, VS_LAYOUT_BSHD, perm, B, S, H, D, softmax_scale, k_mean,
+  return vs::quantize_residual(q, k, v, VS_LAYOUT_BSHD, perm, 0u, B, S, H, D, softmax_scale, k_mean,
+                               v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
+                               stream);
+}
+
+extern "C" int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       int kv_layout, const int32_t* perm, unsigned flags, int B,
+                                       int S, int H, int D, float softmax_scale,
+                                       const float* k_mean, float* v_mean, int vmean_mode,
+                                       uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                                       uint8_t* v8, float* v_scale, float* q_mu, void* stream) {
+  return vs::quantize_residual(q, k, v, kv_layout, perm, flags, B, S, H, D, softmax_scale, k_mean,
                                v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
                                stream);
 }

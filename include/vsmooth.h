@@ -69,6 +69,9 @@ extern "C" {
 /* vs_fp8_attn_fwd flags */
 #define VS_EXPCAST 1u           /* ExpCast-FP8 probability cast              */
 
+/* vs_quantize_residual_ex flags */
+#define VS_QK_HADAMARD 1u       /* rotate Q and centred K by H_D first       */
+
 /* Human-readable name of a return code (static string, never NULL). */
 const char* vs_status_string(int status);
 
@@ -168,6 +171,37 @@ int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
                               int vmean_mode, uint8_t* q8, float* q_scale,
                               uint8_t* k8, float* k_scale, uint8_t* v8,
                               float* v_scale, float* q_mu, void* stream);
+
+/*
+ * vs_quantize_residual_ex -- the quantizers with every option: the grouping
+ * permutation (as vs_quantize_residual_perm) and the QK Hadamard rotation.
+ * Source: VC-Attention summary, Key Contribution 3 (the fused prologue
+ * holds the gather by the permutation and a QK Hadamard rotation) and Main
+ * Findings (rotating Q and K moves PSNR by at most 0.1-0.3 dB).
+ *
+ *   kv_layout     as vs_quantize_residual; must be VS_LAYOUT_BSHD when
+ *                 perm != NULL.
+ *   perm          i32 [B,H,S] or NULL (as vs_quantize_residual_perm).
+ *   flags         0 or VS_QK_HADAMARD: each row of Q and of the centred K
+ *                 is multiplied by the Sylvester Hadamard matrix H_D
+ *                 (entries +-1) in float32 -- butterflies (a+b, a-b) over
+ *                 channel bit 0, 1, ..., log2(D)-1 in that order, one
+ *                 rounding each -- before quantization, and Q's factor
+ *                 c = softmax_scale * log2(e) becomes c / D (exact), so the
+ *                 codes' product is the same score: (Q H / D)(K H)^T = Q K^T.
+ *                 q_mu and lse2 are unchanged (original logits).  V is not
+ *                 rotated.  vs_fp8_attn_fwd takes the outputs as they are.
+ *   all other arguments as vs_quantize_residual.
+ * With perm == NULL and flags == 0 this is vs_quantize_residual.
+ */
+int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, int kv_layout,
+                            const int32_t* perm, unsigned flags, int B, int S,
+                            int H, int D, float softmax_scale,
+                            const float* k_mean, float* v_mean,
+                            int vmean_mode, uint8_t* q8, float* q_scale,
+                            uint8_t* k8, float* k_scale, uint8_t* v8,
+                            float* v_scale, float* q_mu, void* stream);
 
 /*
  * vs_fp8_attn_fwd -- FP8 attention forward with the in-recurrence V-mean

@@ -105,6 +105,13 @@ def test_quant_stats_kmeans_argument_errors(lib):
               fake, fake, fake, fake, fake, fake, None, None) == 2
     assert qp(fake, fake, fake, None, 1, 0, 2, 128, 0.1, None, None, 0,
               fake, fake, fake, fake, fake, fake, None, None) == 0   # empty problem
+    qe = lib.vs_quantize_residual_ex
+    ex = lambda **kw: [fake, fake, fake, kw.get("layout", 0), kw.get("perm", None),  # noqa: E731
+                       kw.get("flags", 0), 1, 300, 2, kw.get("D", 128), 0.1, None, None, 0,
+                       fake, fake, fake, fake, fake, fake, None, None]
+    assert qe(*ex(layout=1, perm=fake)) == 1            # a permutation needs BSHD input
+    assert qe(*ex(flags=2)) == 1                        # no such flag
+    assert qe(*ex(flags=1, D=96)) == 2
     k = lib.vs_kmeans_permute
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, None, fake, 1 << 30, None) == 1
     assert k(fake, fake, 1, 300, 2, 128, 16, 0, fake, fake, fake, fake, fake, 1 << 30, None) == 1
@@ -116,7 +123,7 @@ def test_header_constants_match_the_binding():
     from bit_attention_video_smooth_amd import _abi
     text = open(HEADER).read()
     for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
-                 "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD"]:
+                 "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
 

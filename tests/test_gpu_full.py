@@ -15,14 +15,16 @@ from gpu_util import check_attn, check_intermediates, dev, oracle_head, plan_hea
 pytestmark = pytest.mark.gpu
 
 
-def _run(name, expcast=None):
+def _run(name, expcast=None, qk_hadamard=False):
     import bit_attention_video_smooth_amd as vs
     w = workloads.WORKLOADS[name]
     d = dev()
-    print(f"[full] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={expcast}", flush=True)
+    print(f"[full] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={expcast} "
+          f"qk_hadamard={qk_hadamard}", flush=True)
     q, k, v = workloads.generate(w, device=d)
     ec = w.expcast if expcast is None else expcast
-    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=w.kmeans, expcast=ec)
+    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=w.kmeans, expcast=ec,
+                   qk_hadamard=qk_hadamard)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     # properties on every head
@@ -35,19 +37,20 @@ def _run(name, expcast=None):
     return w, q, k, v, plan, ec
 
 
-@pytest.mark.parametrize("name,expcast,heads,nrows", [
-    ("mid", None, (0, 7), 64),
-    ("live", None, (0, 27, 55), 32),
-    ("grouped", None, (0, 39), 32),
-    ("long", True, (0, 55), 24),
-    ("long", False, (31,), 24),
+@pytest.mark.parametrize("name,expcast,heads,nrows,had", [
+    ("mid", None, (0, 7), 64, False),
+    ("live", None, (0, 27, 55), 32, False),
+    ("grouped", None, (0, 39), 32, False),
+    ("long", True, (0, 55), 24, False),
+    ("long", False, (31,), 24, False),
+    ("live", None, (13,), 32, True),
 ])
-def test_full_size(name, expcast, heads, nrows):
-    w, q, k, v, plan, ec = _run(name, expcast)
+def test_full_size(name, expcast, heads, nrows, had):
+    w, q, k, v, plan, ec = _run(name, expcast, had)
     rows = pipeline.sample_rows(w.S, nrows)
     for h in heads:
         print(f"[full] {name} head {h}: oracle", flush=True)
-        ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=w.kmeans, expcast=ec)
+        ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=w.kmeans, expcast=ec, qk_hadamard=had)
         got = plan_head(plan, 0, h, rows)
         check_intermediates(got, ref, w.S, label=f"{name} h{h}")
         np.testing.assert_allclose(got["q_mu"][rows], ref["q_off"], rtol=1e-5, atol=1e-5)

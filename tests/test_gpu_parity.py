@@ -340,3 +340,31 @@ def test_permutation_reused_across_calls():
         check_attn(got["O"], got["lse2"], ref, label=f"reuse h{h}")
         fresh = oracle_head(q2, k2, v2, 0, h, rows[:1], kmeans_kt=(kc, iters))
         assert not np.array_equal(fresh["perm"], perm)
+
+
+@pytest.mark.parametrize("name,S,D,kmeans_kt", [("tiny", None, None, None),
+                                                ("mid", None, None, None),
+                                                ("r", 300, 64, None), ("r", 129, 128, None),
+                                                ("g", 1500, 128, (16, 3))])
+def test_qk_hadamard(name, S, D, kmeans_kt):
+    """Q and the centred K rotated by H_D in the quantizers (VS_QK_HADAMARD):
+    every code and scale bit-exact with the oracle (the rotation's float32
+    butterflies decided in the same order), attention within the bars."""
+    if name in workloads.WORKLOADS:
+        w = workloads.WORKLOADS[name]
+    elif name == "r":
+        w = workloads.Workload("r", 2, S, 3, D, 41, "offsets",
+                               extra=dict(k_off=3.0, k_off_shared=False, v_off=2.0,
+                                          out_frac=0.01, out_mult=10.0))
+    else:
+        w = workloads.Workload("g", 1, S, 2, D, 43, "mixture", kmeans=kmeans_kt,
+                               extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, qk_hadamard=True, kmeans=kmeans_kt)
+    rows = _rows(w.S, 256)
+    for b in range(w.B):
+        for h in sorted({0, w.H - 1}):
+            ref = oracle_head(q, k, v, b, h, rows, qk_hadamard=True, kmeans_kt=kmeans_kt)
+            got = plan_head(plan, b, h, rows)
+            check_intermediates(got, ref, w.S, label=f"hadamard {name} b{b} h{h}")
+            check_attn(got["O"], got["lse2"], ref, label=f"hadamard {name} b{b} h{h}")
