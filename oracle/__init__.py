@@ -10,6 +10,7 @@ the E4M3 format itself).
 Modules
 -------
 e4m3       OCP FP8 E4M3 ("FN") codec from the format definition.
+fp4        OCP MX FP4 (E2M1) codec and the MXFP4 (E8M0 per 32 tokens) V quantizer.
 smoothing  exact K/V statistics and the per-128-token-block quantizers.
 kmeans     integer Lloyd k-means on V, stable label sort, joint K/V gather.
 grouping   the static spatiotemporal-cube permutation of a video token grid.

@@ -26,7 +26,7 @@ dense attention (tests/test_oracle_pipeline.py).
 """
 import numpy as np
 
-from . import attention, e4m3, kmeans, smoothing
+from . import attention, e4m3, fp4, kmeans, smoothing
 
 BLOCK = 128
 
@@ -37,8 +37,8 @@ def default_scale(D: int) -> np.float32:
 
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
-                            qk_hadamard=False, expcast=False, pcast=None, fp32=True,
-                            scores="mfma"):
+                            qk_hadamard=False, v_format="e4m3", expcast=False, pcast=None,
+                            fp32=True, scores="mfma"):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
@@ -46,7 +46,8 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     permutation of the keys and values instead (a static cube grouping or a
     permutation reused from an earlier call), or None.  qk_hadamard: Q and
     the centred K rotated by H_D before quantization (smoothing docstring).
-    smooth: K
+    v_format: "e4m3" (per-block power-of-two scale) or "mxfp4" (E2M1 codes
+    with an E8M0 scale per 32 tokens and channel, ``fp4``).  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
     scores: "mfma" forms QK^T in the FP8 matrix core's arithmetic (the
     precision in which the kernel decides every P code), "exact" in float64.
@@ -105,7 +106,17 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
         qpre = smoothing.prescale_queries(q, c)
     q_codes, q_scale = smoothing.quantize_blocks(qpre)
     k_codes, k_scale = smoothing.quantize_blocks(kc)
-    v_codes, v_scale = smoothing.quantize_blocks(vr)
+    if v_format == "mxfp4":
+        v_codes, v_exps = fp4.quantize_mxfp4(vr)
+        v_scale = None
+        v_hat = fp4.dequantize_mxfp4(v_codes, v_exps, v_codes.shape[0])
+        v_hat_scale = np.ones(smoothing.n_blocks(S), dtype=np.float32)
+        out["v_exps"] = v_exps
+    elif v_format == "e4m3":
+        v_codes, v_scale = smoothing.quantize_blocks(vr)
+        v_hat, v_hat_scale = e4m3.decode(v_codes), v_scale
+    else:
+        raise ValueError(f"unknown v_format {v_format!r}")
     out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
                k_scale=k_scale, v_codes=v_codes, v_scale=v_scale, q_off=q_off)
 
@@ -113,7 +124,7 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
         pcast = "expcast" if expcast else "e4m3"
     o, lse2 = attention.tiled_attention(
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
-        e4m3.decode(k_codes), k_scale, e4m3.decode(v_codes), v_scale, S, 1.0,
+        e4m3.decode(k_codes), k_scale, v_hat, v_hat_scale, S, 1.0,
         v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
         fp32=fp32, qk_codes=(q_codes[rows], k_codes) if scores == "mfma" else None)
     out["O"], out["lse2"] = o, lse2
