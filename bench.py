@@ -90,6 +90,8 @@ def main():
                          "(grouping amortized away)")
     ap.add_argument("--qk-hadamard", action="store_true",
                     help="rotate Q and the centred K by the Hadamard matrix in the quantizers")
+    ap.add_argument("--v-format", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="V residual format (mxfp4: E2M1 codes, E8M0 scale per 32 tokens)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -115,7 +117,8 @@ def main():
     print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
     q, k, v = workloads.generate(w, device=dev)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
-                   fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard)
+                   fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard,
+                   v_format=args.v_format)
     regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
@@ -165,13 +168,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3",
+        "dtype": "fp8e4m3" if args.v_format == "e4m3" else "fp8e4m3 (V: mxfp4)",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}",
                    "kmeans": list(w.kmeans) if w.kmeans else None, "expcast": expcast,
                    "gather": args.gather if w.kmeans else None,
                    "grouping_per_step": bool(w.kmeans) and regroup,
                    "qk_hadamard": bool(args.qk_hadamard),
+                   "v_format": args.v_format,
                    "smoothing": "K seq-mean centring + V block-mean restore",
                    "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
                    "attn_ms": round(attn_ms, 4),

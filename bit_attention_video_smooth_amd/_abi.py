@@ -10,6 +10,7 @@ VS_LAYOUT_BSHD, VS_LAYOUT_BHSD = 0, 1
 VS_VMEAN_NONE, VS_VMEAN_BLOCK, VS_VMEAN_SEQ, VS_VMEAN_BLOCK_OUT = 0, 1, 2, 3
 VS_EXPCAST = 1
 VS_QK_HADAMARD = 1
+VS_V_MXFP4 = 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

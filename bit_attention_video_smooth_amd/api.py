@@ -15,7 +15,7 @@ import math
 import torch
 
 from . import _abi
-from ._abi import (VS_EXPCAST, VS_QK_HADAMARD, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+from ._abi import (VS_EXPCAST, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
@@ -146,11 +146,14 @@ class Plan:
     cube: ((T, Hg, W), (ct, ch, cw)) groups the tokens by the static
     spatiotemporal-cube permutation instead (formed once, here);
     qk_hadamard: Q and the centred K rotated by the Hadamard matrix before
-    quantization (VS_QK_HADAMARD).
+    quantization (VS_QK_HADAMARD); v_format: "e4m3" or "mxfp4" (the V
+    residual as E2M1 codes with an E8M0 scale per 32 tokens and channel,
+    VS_V_MXFP4: v8 is then u8 [B,H,nb,D,64] and v_scale u8 [B,H,nb,D,4]).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
-                 kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False):
+                 kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False,
+                 v_format="e4m3"):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -158,15 +161,22 @@ class Plan:
         self.smooth = smooth
         self.vmean_mode = _VMEAN[vmean] if smooth else VS_VMEAN_NONE
         self.kmeans = kmeans
-        self.flags = VS_EXPCAST if expcast else 0
-        self.quant_flags = VS_QK_HADAMARD if qk_hadamard else 0
+        if v_format not in ("e4m3", "mxfp4"):
+            raise ValueError(f"unknown v_format {v_format!r}")
+        self.v_format = v_format
+        v4 = VS_V_MXFP4 if v_format == "mxfp4" else 0
+        self.flags = (VS_EXPCAST if expcast else 0) | v4
+        self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4
         nb = (S + 127) // 128
         dev = self.device
         f32, u8, i32 = torch.float32, torch.uint8, torch.int32
         e = lambda *s, dtype=f32: torch.empty(*s, dtype=dtype, device=dev)  # noqa: E731
         self.q8, self.k8 = e(B, H, nb * 128, D, dtype=u8), e(B, H, nb * 128, D, dtype=u8)
-        self.v8 = e(B, H, nb, D, 128, dtype=u8)
-        self.q_scale, self.k_scale, self.v_scale = e(B, H, nb), e(B, H, nb), e(B, H, nb)
+        self.q_scale, self.k_scale = e(B, H, nb), e(B, H, nb)
+        if v4:
+            self.v8, self.v_scale = e(B, H, nb, D, 64, dtype=u8), e(B, H, nb, D, 4, dtype=u8)
+        else:
+            self.v8, self.v_scale = e(B, H, nb, D, 128, dtype=u8), e(B, H, nb)
         self.out, self.lse2 = e(B, S, H, D), e(B, H, S)
         self.k_mean = self.q_mu = self.v_mean = self.stats_ws = None
         if smooth:

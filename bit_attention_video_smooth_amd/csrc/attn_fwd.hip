@@ -121,13 +121,14 @@ __device__ __forceinline__ void dma16(rsrc_t rs, int voff, int soff, void* dst) 
 // Uniform values and per-lane constants of one wave.
 template <int D>
 struct Ctx {
-  rsrc_t krs, vrs, murs;                 // this head's K codes, V codes, V block means
+  rsrc_t krs, vrs, murs, scrs;           // K codes, V codes, V block means, V group scales
   const float* ksc;                      // K block scales of this head
   const float* vsc;                      // V block scales of this head
   int q_e8;                              // E8M0 byte of this query block's scale
   int nb, S, dma_wave, hh, lane;         // dma_wave: 0-3 in the DMA group, else -1
   int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
   int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
+  int v4_rd[2];                          // MXFP4 V: read offset of k-step kk
   v8i qa[D / 64];                        // this lane's query, B operand of QK
   v8i ones;                              // E4M3 ones or zeros, A operand of the row sums
 };
@@ -160,9 +161,12 @@ __device__ __forceinline__ void issue_k(const Ctx<D>& c, int j, uint8_t* dst) {
   }
 }
 
-template <int D, int VMEAN>
-__device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, float* mu_dst) {
-  constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
+// V of tile j (E4M3: 16 KB at D = 128; MXFP4: 8 KB of codes plus the
+// D x 4 group scale bytes), and its block mean.
+template <int D, int VMEAN, bool V4>
+__device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, float* mu_dst,
+                                        uint8_t* sc_dst) {
+  constexpr int TB = kBlock * D / (V4 ? 2 : 1), NDMA = TB / 16 / 64 / 4;
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int base = (c.dma_wave * NDMA + i) * 1024;
@@ -170,6 +174,8 @@ __device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, fl
   }
   if (VMEAN == VS_VMEAN_BLOCK && c.dma_wave == 0 && c.lane < D / 4)
     dma16(c.murs, 16 * c.lane, j * D * 4, mu_dst);
+  if (V4 && c.dma_wave == 1 && c.lane < D / 4)
+    dma16(c.scrs, 16 * c.lane, j * D * 4, sc_dst);
 }
 
 // Keys at or past `valid` (ragged last tile) -> -inf: dropped from the max,
@@ -265,10 +271,10 @@ __device__ __forceinline__ int p_codes4(const v16f& s, int w, float bias) {
 // for tile j - 1 (if j >= 1) the row sums of its E4M3 probabilities, PV and
 // the rank-one mean restore, and l's update.
 //   kb: K of tile j      vb, mub: V and V mean of tile j - 1
-template <int D, int VMEAN>
+template <int D, int VMEAN, bool V4>
 __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D>& st,
                                            const uint8_t* kb, const uint8_t* vb,
-                                           const float* mub) {
+                                           const float* mub, const uint8_t* scb) {
   constexpr int KD = D / 64, DT = D / 32;
   // the matrix-core phase issues first when both waves of the SIMD are ready
   __builtin_amdgcn_s_setprio(1);
@@ -304,13 +310,38 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
       const uint8_t* vr = vb + (i % DT) * 32 * kBlock;
       return make_v8i(lds_read16(vr + c.v_rd[i / DT][0]), lds_read16(vr + c.v_rd[i / DT][1]));
     };
-    v8i vf = vfrag(0);
+    if (V4) {
+      // MXFP4 V^T: lane (channel 32 dt + lane % 32, half hh) holds k-step
+      // kk's tokens 64 kk + 32 hh .. + 31 in 16 bytes, and passes its own
+      // E8M0 group scale (byte 2 kk + hh of its channel's scale word)
+      uint32_t sw[DT];
 #pragma unroll
-    for (int i = 0; i < 2 * DT; ++i) {
-      const v8i a = vf;
-      if (i + 1 < 2 * DT) vf = vfrag(i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      st.acc[i % DT] = mfma_fp8_scaled(a, st.pb[i / DT], st.acc[i % DT], sv_e8, 127 - 8);
+      for (int dt = 0; dt < DT; ++dt)
+        sw[dt] = reinterpret_cast<const uint32_t*>(scb)[32 * dt + (c.lane & 31)] >> (8 * c.hh);
+      auto vfrag4 = [&](int i) {
+        const uint4 x = lds_read16(vb + (i % DT) * 32 * 64 + c.v4_rd[i / DT]);
+        return v8i{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z),
+                   static_cast<int>(x.w), 0, 0, 0, 0};
+      };
+      v8i vf = vfrag4(0);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        const v8i a = vf;
+        if (i + 1 < 2 * DT) vf = vfrag4(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int sa = static_cast<int>((sw[i % DT] >> (16 * (i / DT))) & 0xFF);
+        st.acc[i % DT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a, st.pb[i / DT], st.acc[i % DT], 4, 0, 0, sa, 0, 127 - 8);
+      }
+    } else {
+      v8i vf = vfrag(0);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        const v8i a = vf;
+        if (i + 1 < 2 * DT) vf = vfrag(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        st.acc[i % DT] = mfma_fp8_scaled(a, st.pb[i / DT], st.acc[i % DT], sv_e8, 127 - 8);
+      }
     }
     const float ell = rs[0] * (1.0f / 256.0f);
     if (VMEAN == VS_VMEAN_BLOCK) {
@@ -341,7 +372,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
 #pragma unroll
     for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(st.acc[t]));
     // after the last LDS read of the phase, so no wait joins the two
-    st.vs = c.vsc[j < c.nb ? j : c.nb - 1];
+    if (!V4) st.vs = c.vsc[j < c.nb ? j : c.nb - 1];
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -394,23 +425,24 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D
 // last read in the other group's M(j - 1), which ended at the barrier before.
 //   kb: K_j (read)     kw: K_{j+1} (filled)
 //   vb: V_{j-1} (read) vw: V_j (filled)
-template <int D, bool EXPCAST, int VMEAN>
+template <int D, bool EXPCAST, int VMEAN, bool V4>
 __device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D>& c, State<D>& st,
                                               const uint8_t* kb, uint8_t* kw,
                                               const uint8_t* vb, uint8_t* vw,
-                                              const float* mub, float* muw) {
+                                              const float* mub, float* muw,
+                                              const uint8_t* scb, uint8_t* scw) {
   if (c.dma_wave >= 0 && j < c.nb) {
     if (j + 1 < c.nb) issue_k<D>(c, j + 1, kw);
-    issue_v<D, VMEAN>(c, j, vw, muw);
+    issue_v<D, VMEAN, V4>(c, j, vw, muw, scw);
   }
-  phase_mfma<D, VMEAN>(j, c, st, kb, vb, mub);
+  phase_mfma<D, VMEAN, V4>(j, c, st, kb, vb, mub, scb);
   __syncthreads();
   if (j < c.nb) phase_valu<D, EXPCAST>(j, c, st);
   if (c.dma_wave >= 0) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 
-template <int D, bool EXPCAST, int VMEAN>
+template <int D, bool EXPCAST, int VMEAN, bool V4>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
@@ -429,6 +461,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t sv1[TB];
   __shared__ __attribute__((aligned(16))) float smu0[D];
   __shared__ __attribute__((aligned(16))) float smu1[D];
+  // MXFP4 V: the tile's E8M0 group scales, 4 bytes per channel
+  __shared__ __attribute__((aligned(16))) uint8_t ssc0[V4 ? D * 4 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ssc1[V4 ? D * 4 : 16];
 
   // ---- workgroup -> (b, h, pair of query blocks), XCD-contiguous ----
   int qp, h, b;
@@ -470,15 +505,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   }
   c.q_e8 = e8m0_of(q_scale[bh * nb + qb]);
   c.krs = make_rsrc(k8 + bh * S_pad * D, S_pad * D);
-  c.vrs = make_rsrc(v8 + bh * S_pad * D, S_pad * D);
+  c.vrs = V4 ? make_rsrc(v8 + bh * S_pad * D / 2, S_pad * D / 2)
+             : make_rsrc(v8 + bh * S_pad * D, S_pad * D);
+  c.scrs = make_rsrc(V4 ? reinterpret_cast<const uint8_t*>(v_scale) + bh * nb * D * 4
+                        : reinterpret_cast<const uint8_t*>(v_scale),
+                     V4 ? nb * D * 4 : 0);
   c.murs = make_rsrc(VMEAN == VS_VMEAN_BLOCK ? v_mean + bh * nb * D : v_mean,
                      VMEAN == VS_VMEAN_BLOCK ? nb * D * sizeof(float) : 0);
   c.ksc = k_scale + bh * nb;
   c.vsc = v_scale + bh * nb;
   c.k_src[0] = dma_src_chunk<KRC>(lane, 0) * 16;
   c.k_src[1] = dma_src_chunk<KRC>(lane, 1) * 16;
-  c.v_src[0] = dma_src_chunk<8>(lane, 0) * 16;
-  c.v_src[1] = dma_src_chunk<8>(lane, 1) * 16;
+  c.v_src[0] = dma_src_chunk<V4 ? 4 : 8>(lane, 0) * 16;
+  c.v_src[1] = dma_src_chunk<V4 ? 4 : 8>(lane, 1) * 16;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    c.v4_rd[kk] = l32 * 64 + (((2 * kk + hh) ^ row_swz<4>(l32)) << 4);
 #pragma unroll
   for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
@@ -495,7 +537,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 
   State<D> st;
   st.ks = c.ksc[0];
-  st.vs = c.vsc[0];
+  st.vs = V4 ? 1.0f : c.vsc[0];
   st.m = -INFINITY;
   st.l = 0.0f;
   st.alpha = 1.0f;
@@ -514,9 +556,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 
   // ---- nb + 1 trips, two per loop iteration (static buffer roles) ----
   for (int j = 0; j <= nb; j += 2) {
-    pingpong_trip<D, EXPCAST, VMEAN>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0);
+    pingpong_trip<D, EXPCAST, VMEAN, V4>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0, ssc1, ssc0);
     if (j + 1 <= nb)
-      pingpong_trip<D, EXPCAST, VMEAN>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0, smu1);
+      pingpong_trip<D, EXPCAST, VMEAN, V4>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0, smu1, ssc0,
+                                           ssc1);
   }
   if (group == 0) __syncthreads();
 
@@ -546,21 +589,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   }
 }
 
-template <int D, bool EXPCAST>
+template <int D, bool EXPCAST, bool V4>
 void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
                const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
                const float* vm, const float* qmu, int S, int H, int nb, int npairs,
                float* out, float* lse2) {
   const dim3 grid(total), block(512);
   if (vmean_mode == VS_VMEAN_BLOCK)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK, V4>), grid, block, 0, st, q8,
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
   else if (vmean_mode == VS_VMEAN_SEQ)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ, V4>), grid, block, 0, st, q8,
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE>), grid, block, 0, st, q8, qs, k8,
-                       ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE, V4>), grid, block, 0, st, q8,
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
 }
 
 }  // namespace
@@ -575,7 +618,7 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
     return VS_ERR_INVALID_ARG;
-  if (flags & ~VS_EXPCAST) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_EXPCAST | VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
@@ -593,14 +636,20 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   if (static_cast<long long>(nb) * kBlock * D > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
 
   hipStream_t st = as_stream(stream);
-  const bool ec = (flags & VS_EXPCAST) != 0;
+  const bool ec = (flags & VS_EXPCAST) != 0, v4 = (flags & VS_V_MXFP4) != 0;
   const int tot = static_cast<int>(total);
-  if (D == 128) {
-    if (ec) launch_vm<128, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
-    else launch_vm<128, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
-  } else {
-    if (ec) launch_vm<64, true>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
-    else launch_vm<64, false>(vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, H, nb, npairs, out, lse2);
+#define VS_ATTN_ARGS vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, \
+    H, nb, npairs, out, lse2
+  switch ((D == 128 ? 4 : 0) | (ec ? 2 : 0) | (v4 ? 1 : 0)) {
+    case 0: launch_vm<64, false, false>(VS_ATTN_ARGS); break;
+    case 1: launch_vm<64, false, true>(VS_ATTN_ARGS); break;
+    case 2: launch_vm<64, true, false>(VS_ATTN_ARGS); break;
+    case 3: launch_vm<64, true, true>(VS_ATTN_ARGS); break;
+    case 4: launch_vm<128, false, false>(VS_ATTN_ARGS); break;
+    case 5: launch_vm<128, false, true>(VS_ATTN_ARGS); break;
+    case 6: launch_vm<128, true, false>(VS_ATTN_ARGS); break;
+    default: launch_vm<128, true, true>(VS_ATTN_ARGS); break;
   }
+#undef VS_ATTN_ARGS
   return launch_status();
 }

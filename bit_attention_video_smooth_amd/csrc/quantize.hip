@@ -246,6 +246,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
 }
 
+// OCP MX FP4 (E2M1) nibble of x: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// ties to the even code (mantissa bit 0), saturating at 6, sign kept.
+__device__ __forceinline__ uint32_t fp4_code(float x) {
+  const float m = __builtin_fabsf(x);
+  const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                     (m >= 3.5f) + (m > 5.0f);
+  return c | (__float_as_uint(x) >> 31 << 3);
+}
+
+// Smallest e >= -127 with amax <= 6 * 2^e (0 when amax == 0).
+__device__ __forceinline__ int fp4_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = ilogbf(amax) - 2;
+  while (amax > ldexpf(6.0f, e)) ++e;
+  while (e > -127 && amax <= ldexpf(6.0f, e - 1)) --e;
+  return e < -127 ? -127 : e;
+}
+
 // Columns k of the 4x4 byte matrix whose rows are w[0..3]: byte k of the
 // result e is byte e of w[k] (two rounds of v_perm_b32).
 __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&col)[4]) {
@@ -272,7 +290,16 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
 // per thread, then over the threads of a channel group in a fixed order, one
 // division, one rounding to float32, as vs_smooth_stats forms it -- written
 // to v_mean and subtracted.
-template <int D, bool OWN_MEAN, bool PERM>
+//
+// FP4 (VS_V_MXFP4): the residual as OCP MX FP4 (E2M1) codes with one E8M0
+// scale per channel and 32 consecutive tokens (group g = tokens 32g..32g+31
+// of the block), the smallest power of two 2^e (e >= -127) with
+// amax <= 6 * 2^e; codes round to nearest even (fp4_code).  Per block a
+// D x 64-byte tile: channel row d holds group g in bytes 16g..16g+15, in
+// the k order of the 4-bit A operand of the FP8/FP4 matrix core -- nibble
+// q (low nibble first) is token 8 ((q % 16) / 4) + 4 (q / 16) + q % 4 of
+// the group -- and scale_out is u8 [B,H,nb,D,4], byte g = e + 127.
+template <int D, bool OWN_MEAN, bool PERM, bool FP4>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
@@ -356,6 +383,54 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
           if (j * kBlock + 4 * (a0 + QR * n) + q < S) val[n][q][e] -= m;
     }
   }
+  if constexpr (FP4) {
+    // group maxima (float bits of non-negative values order as integers);
+    // a quad of tokens 4a..4a+3 lies in group a / 8
+    __shared__ unsigned gmax[4][D];
+    __shared__ int gexp[4][D];
+    uint8_t* tile4 = tile;                       // D x 64 bytes of the tile
+    for (int i = threadIdx.x; i < 4 * D; i += 256) (&gmax[0][0])[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int g = (a0 + QR * n) >> 3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(val[n][q][e]));
+        atomicMax(&gmax[g][8 * c + e], __float_as_uint(m));
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * D; i += 256) {
+      const int g = i / D, d = i % D;
+      const int ex = fp4_exponent(__uint_as_float(gmax[g][d]));
+      gexp[g][d] = ex;
+      reinterpret_cast<uint8_t*>(scale_out)[((bh * nb + j) * D + d) * 4 + g] =
+          static_cast<uint8_t>(ex + 127);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int a = a0 + QR * n, g = a >> 3;
+      // the quad's four nibbles: bytes 8 (a % 2) + 2 ((a % 8) / 2) of the group
+      const int off = 16 * g + 8 * (a & 1) + 2 * ((a & 7) >> 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float inv = ldexpf(1.0f, -gexp[g][8 * c + e]);
+        uint32_t w = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w |= fp4_code(val[n][q][e] * inv) << (4 * q);
+        *reinterpret_cast<uint16_t*>(tile4 + (8 * c + e) * 64 + off) = static_cast<uint16_t>(w);
+      }
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(codes + (bh * nb + j) * static_cast<size_t>(D) * 64);
+    for (int idx = threadIdx.x; idx < D * 64 / 16; idx += 256)
+      dst[idx] = *reinterpret_cast<const uint4*>(tile4 + 16 * idx);
+    return;
+  }
   float a = 0.0f;
 #pragma unroll
   for (int n = 0; n < NQ; ++n)
@@ -404,7 +479,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
 namespace vs {
 namespace {
 
-template <int D, bool PERM, bool HAD>
+template <int D, bool PERM, bool HAD, bool FP4>
 void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, const uint16_t* q,
                   const uint16_t* k, const uint16_t* v, int kv_layout, int S, int H, int nb,
                   float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
@@ -419,11 +494,11 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
   hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD>), gkv.grid, block, 0, st, k, kv_layout, S,
                      H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
   if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-    hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM>), gkv.grid, block, 0, st, v, kv_layout, S,
-                       H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+    hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM, FP4>), gkv.grid, block, 0, st, v, kv_layout,
+                       S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
   else
-    hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM>), gkv.grid, block, 0, st, v, kv_layout, S,
-                       H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+    hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM, FP4>), gkv.grid, block, 0, st, v,
+                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
 }
 
 int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, int kv_layout,
@@ -435,7 +510,7 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (perm && kv_layout != VS_LAYOUT_BSHD) return VS_ERR_INVALID_ARG;
-  if (flags & ~VS_QK_HADAMARD) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_QK_HADAMARD | VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
       vmean_mode != VS_VMEAN_BLOCK_OUT)
     return VS_ERR_INVALID_ARG;
@@ -457,13 +532,26 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
 #define VS_QUANT_ARGS gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean, \
     vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm
-  const bool had = (flags & VS_QK_HADAMARD) != 0;
-  if (D == 128) {
-    if (perm) had ? launch_quant<128, true, true>(VS_QUANT_ARGS) : launch_quant<128, true, false>(VS_QUANT_ARGS);
-    else had ? launch_quant<128, false, true>(VS_QUANT_ARGS) : launch_quant<128, false, false>(VS_QUANT_ARGS);
-  } else {
-    if (perm) had ? launch_quant<64, true, true>(VS_QUANT_ARGS) : launch_quant<64, true, false>(VS_QUANT_ARGS);
-    else had ? launch_quant<64, false, true>(VS_QUANT_ARGS) : launch_quant<64, false, false>(VS_QUANT_ARGS);
+  const bool had = (flags & VS_QK_HADAMARD) != 0, fp4 = (flags & VS_V_MXFP4) != 0;
+  // (D, permutation, rotation, FP4 V) -> one instantiation
+  const int sel = (D == 128 ? 8 : 0) | (perm ? 4 : 0) | (had ? 2 : 0) | (fp4 ? 1 : 0);
+  switch (sel) {
+    case 0: launch_quant<64, false, false, false>(VS_QUANT_ARGS); break;
+    case 1: launch_quant<64, false, false, true>(VS_QUANT_ARGS); break;
+    case 2: launch_quant<64, false, true, false>(VS_QUANT_ARGS); break;
+    case 3: launch_quant<64, false, true, true>(VS_QUANT_ARGS); break;
+    case 4: launch_quant<64, true, false, false>(VS_QUANT_ARGS); break;
+    case 5: launch_quant<64, true, false, true>(VS_QUANT_ARGS); break;
+    case 6: launch_quant<64, true, true, false>(VS_QUANT_ARGS); break;
+    case 7: launch_quant<64, true, true, true>(VS_QUANT_ARGS); break;
+    case 8: launch_quant<128, false, false, false>(VS_QUANT_ARGS); break;
+    case 9: launch_quant<128, false, false, true>(VS_QUANT_ARGS); break;
+    case 10: launch_quant<128, false, true, false>(VS_QUANT_ARGS); break;
+    case 11: launch_quant<128, false, true, true>(VS_QUANT_ARGS); break;
+    case 12: launch_quant<128, true, false, false>(VS_QUANT_ARGS); break;
+    case 13: launch_quant<128, true, false, true>(VS_QUANT_ARGS); break;
+    case 14: launch_quant<128, true, true, false>(VS_QUANT_ARGS); break;
+    default: launch_quant<128, true, true, true>(VS_QUANT_ARGS); break;
   }
 #undef VS_QUANT_ARGS
   return launch_status();

@@ -71,6 +71,8 @@ extern "C" {
 
 /* vs_quantize_residual_ex flags */
 #define VS_QK_HADAMARD 1u       /* rotate Q and centred K by H_D first       */
+/* vs_quantize_residual_ex and vs_fp8_attn_fwd flag */
+#define VS_V_MXFP4 2u           /* V residual as MXFP4 (E2M1, E8M0 per 32)   */
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* vs_status_string(int status);
@@ -191,6 +193,19 @@ int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
  *                 codes' product is the same score: (Q H / D)(K H)^T = Q K^T.
  *                 q_mu and lse2 are unchanged (original logits).  V is not
  *                 rotated.  vs_fp8_attn_fwd takes the outputs as they are.
+ *                 | VS_V_MXFP4: the V residual as OCP MX FP4 -- E2M1 codes
+ *                 (0, 0.5, 1, 1.5, 2, 3, 4, 6, signed; nearest, ties to the
+ *                 even code) with one E8M0 scale 2^e per channel and 32
+ *                 consecutive tokens of a block (group g = tokens
+ *                 32g..32g+31), e the smallest integer >= -127 with
+ *                 amax <= 6 * 2^e (0 for an all-zero group).  v8 is then
+ *                 u8 [B,H,nb,D,64]: channel row d of block j holds group g in
+ *                 bytes 16g..16g+15, nibble q (low nibble first) = token
+ *                 32g + 8*((q%16)/4) + 4*(q/16) + q%4 (the k order of
+ *                 gfx950's 4-bit matrix-core A operand); v_scale is u8
+ *                 [B,H,nb,D,4], byte g = e + 127.  Source: VC-Attention
+ *                 summary (V-Smooth with 4-bit operands; the pages' NVFP4
+ *                 read as gfx950's MX FP4).
  *   all other arguments as vs_quantize_residual.
  * With perm == NULL and flags == 0 this is vs_quantize_residual.
  */
@@ -218,7 +233,10 @@ int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k,
  *                 ([B,H,nb,D] for VS_VMEAN_BLOCK, [B,H,D] for VS_VMEAN_SEQ),
  *                 NULL with VS_VMEAN_NONE.
  *   q_mu          f32 [B,H,S] or NULL (then 0).
- *   flags         0 or VS_EXPCAST.
+ *   flags         VS_EXPCAST and/or VS_V_MXFP4 (v8 and v_scale in the
+ *                 MXFP4 layout of vs_quantize_residual_ex; the PV product
+ *                 then takes 4-bit V codes with their per-lane group
+ *                 scales).
  *   out           out f32 [B,S,H,D]: attention output in the caller's
  *                 query order.
  *   lse2          out f32 [B,H,S]: log2 sum_t 2^(c * score_t) of the

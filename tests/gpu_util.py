@@ -62,16 +62,38 @@ def check_attn(o_gpu, lse_gpu, ref, label=""):
     return e
 
 
+def v4_rows(v8_head, vsc_head):
+    """MXFP4 V of one head: ([nb, D, 64] nibble tiles, [nb, D, 4] E8M0 bytes)
+    -> (codes [nb*128, D], exponents [nb*4, D]) in token order (the layout
+    vsmooth.h documents for VS_V_MXFP4)."""
+    nb, D, _ = v8_head.shape
+    codes = np.zeros((nb * 128, D), dtype=np.uint8)
+    q = np.arange(32)
+    u = 8 * ((q % 16) // 4) + 4 * (q // 16) + q % 4
+    for j in range(nb):
+        for g in range(4):
+            byts = v8_head[j, :, 16 * g:16 * g + 16]          # [D, 16]
+            nib = np.stack([byts & 15, byts >> 4], axis=-1).reshape(D, 32)
+            codes[j * 128 + 32 * g + u, :] = nib.T
+    exps = vsc_head.astype(np.int32).transpose(0, 2, 1).reshape(nb * 4, D) - 127
+    return codes, exps
+
+
 def plan_head(plan, b, h, rows):
     """GPU outputs of one head: O rows, lse2 rows and the intermediates."""
     S = plan.shape[1]
     g = lambda t: None if t is None else t[b, h].cpu().numpy()  # noqa: E731
     out = {"O": plan.out[b, :, h, :].cpu().numpy()[rows],
            "lse2": plan.lse2[b, h].cpu().numpy()[rows],
-           "q_codes": g(plan.q8), "k_codes": g(plan.k8), "v_codes": v8_rows(g(plan.v8)),
+           "q_codes": g(plan.q8), "k_codes": g(plan.k8),
            "q_scale": g(plan.q_scale), "k_scale": g(plan.k_scale), "v_scale": g(plan.v_scale),
            "k_mean": g(plan.k_mean), "v_mean": g(plan.v_mean),
            "q_mu": None if plan.q_mu is None else plan.q_mu[b, h].cpu().numpy()}
+    if getattr(plan, "v_format", "e4m3") == "mxfp4":
+        out["v_codes"], out["v_exps"] = v4_rows(g(plan.v8), g(plan.v_scale))
+        out["v_scale"] = None
+    else:
+        out["v_codes"] = v8_rows(g(plan.v8))
     if plan.labels is not None:
         out["labels"] = g(plan.labels)
         out["perm"] = g(plan.perm)
@@ -86,7 +108,10 @@ def check_intermediates(gpu, ref, S, label=""):
     """Statistics and codes bit-exact; q_mu to float32 summation error."""
     np.testing.assert_array_equal(gpu["q_scale"], ref["q_scale"], err_msg=label + " q_scale")
     np.testing.assert_array_equal(gpu["k_scale"], ref["k_scale"], err_msg=label + " k_scale")
-    np.testing.assert_array_equal(gpu["v_scale"], ref["v_scale"], err_msg=label + " v_scale")
+    if ref.get("v_exps") is not None:
+        np.testing.assert_array_equal(gpu["v_exps"], ref["v_exps"], err_msg=label + " v_exps")
+    else:
+        np.testing.assert_array_equal(gpu["v_scale"], ref["v_scale"], err_msg=label + " v_scale")
     np.testing.assert_array_equal(gpu["q_codes"], ref["q_codes"], err_msg=label + " q codes")
     np.testing.assert_array_equal(gpu["k_codes"], ref["k_codes"], err_msg=label + " k codes")
     np.testing.assert_array_equal(gpu["v_codes"], ref["v_codes"], err_msg=label + " v codes")

@@ -70,6 +70,7 @@ def test_attn_argument_errors(lib):
     assert f(*args(mode=1)) == 1                      # block mean without a buffer
     assert f(*args(mode=7, vm=fake)) == 1
     assert f(*args(flags=4)) == 1
+    assert f(*args(flags=3, D=96)) == 2                # ExpCast with MXFP4 V: a valid flag pair
     assert f(*args(q8=ctypes.c_void_p(0x1004))) == 2  # misaligned
     assert f(*args(S=0)) == 0                         # empty problem
     assert f(*args(S=0, D=96)) == 2
@@ -110,7 +111,7 @@ def test_quant_stats_kmeans_argument_errors(lib):
                        kw.get("flags", 0), 1, 300, 2, kw.get("D", 128), 0.1, None, None, 0,
                        fake, fake, fake, fake, fake, fake, None, None]
     assert qe(*ex(layout=1, perm=fake)) == 1            # a permutation needs BSHD input
-    assert qe(*ex(flags=2)) == 1                        # no such flag
+    assert qe(*ex(flags=4)) == 1                        # no such flag
     assert qe(*ex(flags=1, D=96)) == 2
     k = lib.vs_kmeans_permute
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, None, fake, 1 << 30, None) == 1
@@ -123,7 +124,8 @@ def test_header_constants_match_the_binding():
     from bit_attention_video_smooth_amd import _abi
     text = open(HEADER).read()
     for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
-                 "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD"]:
+                 "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD",
+                 "VS_V_MXFP4"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
 

@@ -4,7 +4,7 @@ the unsmoothed FP8 path, at the five workloads' full sizes (TeleFuser PR
 output error).  Reported per workload and head: relative L2, MSE, cosine
 and SQNR of O with smoothing on and off; for the ExpCast workload also the
 smoothed path with ExpCast off; the smoothed path with the QK Hadamard
-rotation; for the video-grid workloads also the
+rotation; smoothed and unsmoothed with the V residual in MXFP4; for the video-grid workloads also the
 smoothed path grouped by the static 2x8x8 spatiotemporal cube instead; the
 share of V energy the block means remove in sequence order, k-means order
 and cube order (VC-Attention summary, Main Findings), from the oracle's own
@@ -27,13 +27,13 @@ OFFSET_K = {"tiny", "mid"}
 CUBE = (2, 8, 8)
 
 
-def _outputs(w, q, k, v, smooth, expcast=None, cube=None, qk_hadamard=False):
+def _outputs(w, q, k, v, smooth, expcast=None, cube=None, qk_hadamard=False, v_format="e4m3"):
     import bit_attention_video_smooth_amd as vs
     d = dev()
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, smooth=smooth,
                    kmeans=w.kmeans if smooth and cube is None else None,
                    expcast=w.expcast if expcast is None else expcast, cube=cube,
-                   qk_hadamard=qk_hadamard)
+                   qk_hadamard=qk_hadamard, v_format=v_format)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     return plan.out
@@ -50,6 +50,8 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
     if w.expcast:
         cases["smoothed, ExpCast off"] = _outputs(w, q, k, v, True, expcast=False)
     cases["smoothed, QK Hadamard"] = _outputs(w, q, k, v, True, qk_hadamard=True)
+    cases["smoothed, MXFP4 V"] = _outputs(w, q, k, v, True, v_format="mxfp4")
+    cases["unsmoothed, MXFP4 V"] = _outputs(w, q, k, v, False, v_format="mxfp4")
     grid = w.extra.get("grid")
     if grid is not None:
         cases["smoothed, cube grouping"] = _outputs(w, q, k, v, True, cube=(grid, CUBE))

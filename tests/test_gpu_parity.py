@@ -368,3 +368,51 @@ def test_qk_hadamard(name, S, D, kmeans_kt):
             got = plan_head(plan, b, h, rows)
             check_intermediates(got, ref, w.S, label=f"hadamard {name} b{b} h{h}")
             check_attn(got["O"], got["lse2"], ref, label=f"hadamard {name} b{b} h{h}")
+
+
+@pytest.mark.parametrize("name,S,D,kmeans_kt,expcast,had", [
+    ("tiny", None, None, None, False, False),
+    ("mid", None, None, None, False, False),
+    ("r", 300, 64, None, True, False),
+    ("r", 129, 128, None, False, True),
+    ("g", 1500, 128, (16, 3), False, False),
+])
+def test_mxfp4_v(name, S, D, kmeans_kt, expcast, had):
+    """V residual as MXFP4 (VS_V_MXFP4): every E2M1 code and E8M0 group
+    exponent bit-exact with the oracle, attention (4-bit V in PV, per-lane
+    group scales) within the bars against the oracle's MXFP4 recurrence."""
+    if name in workloads.WORKLOADS:
+        w = workloads.WORKLOADS[name]
+    elif name == "r":
+        w = workloads.Workload("r", 2, S, 3, D, 47, "offsets",
+                               extra=dict(k_off=3.0, k_off_shared=False, v_off=2.0,
+                                          out_frac=0.01, out_mult=10.0))
+    else:
+        w = workloads.Workload("g", 1, S, 2, D, 49, "mixture", kmeans=kmeans_kt,
+                               extra=dict(n_comp=16, comp_std=3.0, noise=0.5))
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, v_format="mxfp4", kmeans=kmeans_kt, expcast=expcast,
+                    qk_hadamard=had)
+    rows = _rows(w.S, 256)
+    for b in range(w.B):
+        for h in sorted({0, w.H - 1}):
+            ref = oracle_head(q, k, v, b, h, rows, v_format="mxfp4", kmeans_kt=kmeans_kt,
+                              expcast=expcast, qk_hadamard=had)
+            got = plan_head(plan, b, h, rows)
+            check_intermediates(got, ref, w.S, label=f"mxfp4 {name} b{b} h{h}")
+            check_attn(got["O"], got["lse2"], ref, label=f"mxfp4 {name} b{b} h{h}")
+
+
+def test_mxfp4_v_unsmoothed_and_seq_mean():
+    """MXFP4 V without smoothing and with the sequence-mean variant."""
+    w = workloads.WORKLOADS["tiny"]
+    q, k, v = workloads.generate(w)
+    rows = _rows(w.S, 256)
+    for smooth, vmean in ((False, "block"), (True, "seq")):
+        plan = run_plan(q, k, v, v_format="mxfp4", smooth=smooth, vmean=vmean)
+        for h in range(w.H):
+            ref = oracle_head(q, k, v, 0, h, rows, v_format="mxfp4", smooth=smooth,
+                              vmean_mode=vmean)
+            got = plan_head(plan, 0, h, rows)
+            check_intermediates(got, ref, w.S, label=f"mxfp4 smooth{smooth} {vmean} h{h}")
+            check_attn(got["O"], got["lse2"], ref, label=f"mxfp4 smooth{smooth} {vmean} h{h}")
