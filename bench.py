@@ -28,15 +28,16 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_live_traffic.json")
 
 
-def _traffic(workload, expcast):
+def _traffic(workload, expcast, v_format="e4m3"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     record (FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB copy), or None when the
-    record is for another workload or the kernel sources changed since."""
+    record is for another workload or kernel variant, or the kernel sources
+    changed since."""
     import hashlib
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
-        if rec.get("workload") != workload or expcast:
+        if rec.get("workload") != workload or expcast or v_format != "e4m3":
             return None
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -183,7 +184,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(w.name, expcast)},
+                     "traffic": _traffic(w.name, expcast, args.v_format)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
