@@ -15,16 +15,17 @@ from gpu_util import check_attn, check_intermediates, dev, oracle_head, plan_hea
 pytestmark = pytest.mark.gpu
 
 
-def _run(name, expcast=None, qk_hadamard=False):
+def _run(name, expcast=None, opts=None):
     import bit_attention_video_smooth_amd as vs
     w = workloads.WORKLOADS[name]
     d = dev()
+    opts = dict(opts or {})
     print(f"[full] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={expcast} "
-          f"qk_hadamard={qk_hadamard}", flush=True)
+          f"{opts}", flush=True)
     q, k, v = workloads.generate(w, device=d)
     ec = w.expcast if expcast is None else expcast
-    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=w.kmeans, expcast=ec,
-                   qk_hadamard=qk_hadamard)
+    kmeans = None if "cube" in opts else w.kmeans
+    plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=kmeans, expcast=ec, **opts)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     # properties on every head
@@ -32,26 +33,43 @@ def _run(name, expcast=None, qk_hadamard=False):
     if plan.perm is not None:
         srt = torch.sort(plan.perm, dim=-1).values
         assert torch.equal(srt, torch.arange(w.S, device=d, dtype=srt.dtype).expand_as(srt))
-        lab_sorted = torch.gather(plan.labels, -1, plan.perm.long())
-        assert bool((lab_sorted[..., 1:] >= lab_sorted[..., :-1]).all())
+        if plan.labels is not None:
+            lab_sorted = torch.gather(plan.labels, -1, plan.perm.long())
+            assert bool((lab_sorted[..., 1:] >= lab_sorted[..., :-1]).all())
     return w, q, k, v, plan, ec
 
 
-@pytest.mark.parametrize("name,expcast,heads,nrows,had", [
-    ("mid", None, (0, 7), 64, False),
-    ("live", None, (0, 27, 55), 32, False),
-    ("grouped", None, (0, 39), 32, False),
-    ("long", True, (0, 55), 24, False),
-    ("long", False, (31,), 24, False),
-    ("live", None, (13,), 32, True),
+LIVE_CUBE = ((20, 48, 34), (2, 8, 8))
+
+
+@pytest.mark.parametrize("name,expcast,heads,nrows,opts", [
+    ("mid", None, (0, 7), 64, None),
+    ("live", None, (0, 27, 55), 32, None),
+    ("grouped", None, (0, 39), 32, None),
+    ("long", True, (0, 55), 24, None),
+    ("long", False, (31,), 24, None),
+    ("live", None, (13,), 32, {"qk_hadamard": True}),
+    ("live", None, (41,), 32, {"v_format": "mxfp4"}),
+    ("grouped", None, (7,), 32, {"v_format": "mxfp4"}),
+    ("live", None, (50,), 32, {"cube": LIVE_CUBE}),
 ])
-def test_full_size(name, expcast, heads, nrows, had):
-    w, q, k, v, plan, ec = _run(name, expcast, had)
+def test_full_size(name, expcast, heads, nrows, opts):
+    w, q, k, v, plan, ec = _run(name, expcast, opts)
     rows = pipeline.sample_rows(w.S, nrows)
+    opts = dict(opts or {})
+    kw = {"qk_hadamard": opts.get("qk_hadamard", False),
+          "v_format": opts.get("v_format", "e4m3")}
+    if "cube" in opts:
+        from oracle import grouping
+        kw["perm"] = grouping.cube_permutation(w.S, *opts["cube"])
+    else:
+        kw["kmeans_kt"] = w.kmeans
     for h in heads:
         print(f"[full] {name} head {h}: oracle", flush=True)
-        ref = oracle_head(q, k, v, 0, h, rows, kmeans_kt=w.kmeans, expcast=ec, qk_hadamard=had)
+        ref = oracle_head(q, k, v, 0, h, rows, expcast=ec, **kw)
         got = plan_head(plan, 0, h, rows)
+        if "perm" in kw:
+            np.testing.assert_array_equal(plan.perm[0, h].cpu().numpy(), kw["perm"])
         check_intermediates(got, ref, w.S, label=f"{name} h{h}")
         np.testing.assert_allclose(got["q_mu"][rows], ref["q_off"], rtol=1e-5, atol=1e-5)
         check_attn(got["O"], got["lse2"], ref, label=f"{name} ec={ec} h{h}")
