@@ -11,6 +11,7 @@ VS_VMEAN_NONE, VS_VMEAN_BLOCK, VS_VMEAN_SEQ, VS_VMEAN_BLOCK_OUT = 0, 1, 2, 3
 VS_EXPCAST = 1
 VS_QK_HADAMARD = 1
 VS_V_MXFP4 = 2
+VS_OUT_BF16 = 4
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

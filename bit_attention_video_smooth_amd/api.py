@@ -15,7 +15,7 @@ import math
 import torch
 
 from . import _abi
-from ._abi import (VS_EXPCAST, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
@@ -148,12 +148,13 @@ class Plan:
     qk_hadamard: Q and the centred K rotated by the Hadamard matrix before
     quantization (VS_QK_HADAMARD); v_format: "e4m3" or "mxfp4" (the V
     residual as E2M1 codes with an E8M0 scale per 32 tokens and channel,
-    VS_V_MXFP4: v8 is then u8 [B,H,nb,D,64] and v_scale u8 [B,H,nb,D,4]).
+    VS_V_MXFP4: v8 is then u8 [B,H,nb,D,64] and v_scale u8 [B,H,nb,D,4]);
+    out_dtype: torch.float32 or torch.bfloat16 (VS_OUT_BF16).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
                  kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False,
-                 v_format="e4m3"):
+                 v_format="e4m3", out_dtype=torch.float32):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -165,7 +166,10 @@ class Plan:
             raise ValueError(f"unknown v_format {v_format!r}")
         self.v_format = v_format
         v4 = VS_V_MXFP4 if v_format == "mxfp4" else 0
-        self.flags = (VS_EXPCAST if expcast else 0) | v4
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+        self.flags = ((VS_EXPCAST if expcast else 0) | v4 |
+                      (VS_OUT_BF16 if out_dtype == torch.bfloat16 else 0))
         self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4
         nb = (S + 127) // 128
         dev = self.device
@@ -177,7 +181,7 @@ class Plan:
             self.v8, self.v_scale = e(B, H, nb, D, 64, dtype=u8), e(B, H, nb, D, 4, dtype=u8)
         else:
             self.v8, self.v_scale = e(B, H, nb, D, 128, dtype=u8), e(B, H, nb)
-        self.out, self.lse2 = e(B, S, H, D), e(B, H, S)
+        self.out, self.lse2 = e(B, S, H, D, dtype=out_dtype), e(B, H, S)
         self.k_mean = self.q_mu = self.v_mean = self.stats_ws = None
         if smooth:
             self.k_mean = e(B, H, D)

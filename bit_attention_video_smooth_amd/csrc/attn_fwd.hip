@@ -56,6 +56,7 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 constexpr float kExpcastK0 = 119.66015f;   // 120 - 4 (log2(1.5) - 1/2)
 
 typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   v8i r;
@@ -448,7 +449,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, const float* __restrict__ q_mu, int S, int H,
-    int nb, int npairs, int total, float* __restrict__ out, float* __restrict__ lse2) {
+    int nb, int npairs, int total, void* __restrict__ out, int out_bf16,
+    float* __restrict__ lse2) {
   constexpr int KD = D / 64;                 // k-steps of the QK product
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
   constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   // ---- epilogue: O = acc / l (+ sequence mean), lse2 = m + log2 l + q_mu ----
   if (qb_raw < nb && qrow < S) {
     const float inv_l = 1.0f / st.l;
-    float* orow = out + ((static_cast<size_t>(b) * S + qrow) * H + h) * D;
+    const size_t orow = ((static_cast<size_t>(b) * S + qrow) * H + h) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -581,7 +583,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
           const float* mu = v_mean + bh * D + d0;
           o.x += mu[0]; o.y += mu[1]; o.z += mu[2]; o.w += mu[3];
         }
-        *reinterpret_cast<float4*>(orow + d0) = o;
+        if (out_bf16) {
+          // the float32 result rounded to bf16 (nearest even), 8 bytes
+          const v2bf lo = {static_cast<__bf16>(o.x), static_cast<__bf16>(o.y)};
+          const v2bf hi = {static_cast<__bf16>(o.z), static_cast<__bf16>(o.w)};
+          uint2 w;
+          __builtin_memcpy(&w.x, &lo, 4);
+          __builtin_memcpy(&w.y, &hi, 4);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + d0) = o;
+        }
       }
     if (hh == 0)
       lse2[bh * S + qrow] =
@@ -593,17 +605,17 @@ template <int D, bool EXPCAST, bool V4>
 void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
                const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
                const float* vm, const float* qmu, int S, int H, int nb, int npairs,
-               float* out, float* lse2) {
+               void* out, int out_bf16, float* lse2) {
   const dim3 grid(total), block(512);
   if (vmean_mode == VS_VMEAN_BLOCK)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
   else if (vmean_mode == VS_VMEAN_SEQ)
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, lse2);
+                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
 }
 
 }  // namespace
@@ -612,13 +624,13 @@ void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, con
 extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                                const float* k_scale, const uint8_t* v8, const float* v_scale,
                                const float* v_mean, int vmean_mode, const float* q_mu, int B,
-                               int S, int H, int D, unsigned flags, float* out, float* lse2,
+                               int S, int H, int D, unsigned flags, void* out, float* lse2,
                                void* stream) {
   using namespace vs;
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
     return VS_ERR_INVALID_ARG;
-  if (flags & ~(VS_EXPCAST | VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_EXPCAST | VS_V_MXFP4 | VS_OUT_BF16)) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
@@ -638,8 +650,9 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
   hipStream_t st = as_stream(stream);
   const bool ec = (flags & VS_EXPCAST) != 0, v4 = (flags & VS_V_MXFP4) != 0;
   const int tot = static_cast<int>(total);
+  const int out_bf16 = (flags & VS_OUT_BF16) != 0;
 #define VS_ATTN_ARGS vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, \
-    H, nb, npairs, out, lse2
+    H, nb, npairs, out, out_bf16, lse2
   switch ((D == 128 ? 4 : 0) | (ec ? 2 : 0) | (v4 ? 1 : 0)) {
     case 0: launch_vm<64, false, false>(VS_ATTN_ARGS); break;
     case 1: launch_vm<64, false, true>(VS_ATTN_ARGS); break;

@@ -73,6 +73,8 @@ extern "C" {
 #define VS_QK_HADAMARD 1u       /* rotate Q and centred K by H_D first       */
 /* vs_quantize_residual_ex and vs_fp8_attn_fwd flag */
 #define VS_V_MXFP4 2u           /* V residual as MXFP4 (E2M1, E8M0 per 32)   */
+/* vs_fp8_attn_fwd flag */
+#define VS_OUT_BF16 4u          /* attention output in bf16 instead of f32   */
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* vs_status_string(int status);
@@ -233,12 +235,13 @@ int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k,
  *                 ([B,H,nb,D] for VS_VMEAN_BLOCK, [B,H,D] for VS_VMEAN_SEQ),
  *                 NULL with VS_VMEAN_NONE.
  *   q_mu          f32 [B,H,S] or NULL (then 0).
- *   flags         VS_EXPCAST and/or VS_V_MXFP4 (v8 and v_scale in the
+ *   flags         any of VS_EXPCAST, VS_V_MXFP4 (v8 and v_scale in the
  *                 MXFP4 layout of vs_quantize_residual_ex; the PV product
  *                 then takes 4-bit V codes with their per-lane group
- *                 scales).
- *   out           out f32 [B,S,H,D]: attention output in the caller's
- *                 query order.
+ *                 scales), VS_OUT_BF16.
+ *   out           out f32 [B,S,H,D] (bf16 [B,S,H,D] with VS_OUT_BF16: the
+ *                 float32 result rounded to nearest even): attention output
+ *                 in the caller's query order.
  *   lse2          out f32 [B,H,S]: log2 sum_t 2^(c * score_t) of the
  *                 (uncentred) logits: m + log2(l) + q_mu.
  * Non-causal full attention; keys past S are masked.  Per 128-key tile:
@@ -257,7 +260,7 @@ int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                     const float* k_scale, const uint8_t* v8,
                     const float* v_scale, const float* v_mean, int vmean_mode,
                     const float* q_mu, int B, int S, int H, int D,
-                    unsigned flags, float* out, float* lse2, void* stream);
+                    unsigned flags, void* out, float* lse2, void* stream);
 
 /*
  * vs_kmeans_permute -- V-Smooth grouping: integer k-means over each head's V

@@ -69,7 +69,8 @@ def test_attn_argument_errors(lib):
     assert f(*args(B=-1)) == 1
     assert f(*args(mode=1)) == 1                      # block mean without a buffer
     assert f(*args(mode=7, vm=fake)) == 1
-    assert f(*args(flags=4)) == 1
+    assert f(*args(flags=8)) == 1
+    assert f(*args(flags=4, D=96)) == 2                # bf16 output: a valid flag
     assert f(*args(flags=3, D=96)) == 2                # ExpCast with MXFP4 V: a valid flag pair
     assert f(*args(q8=ctypes.c_void_p(0x1004))) == 2  # misaligned
     assert f(*args(S=0)) == 0                         # empty problem
@@ -125,7 +126,7 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
                  "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD",
-                 "VS_V_MXFP4"]:
+                 "VS_V_MXFP4", "VS_OUT_BF16"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
 

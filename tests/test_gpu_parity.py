@@ -416,3 +416,18 @@ def test_mxfp4_v_unsmoothed_and_seq_mean():
             got = plan_head(plan, 0, h, rows)
             check_intermediates(got, ref, w.S, label=f"mxfp4 smooth{smooth} {vmean} h{h}")
             check_attn(got["O"], got["lse2"], ref, label=f"mxfp4 smooth{smooth} {vmean} h{h}")
+
+
+@pytest.mark.parametrize("name,opts", [("tiny", {}), ("mid", {}), ("mid", {"vmean": "seq"}),
+                                       ("tiny", {"v_format": "mxfp4", "expcast": True})])
+def test_bf16_output_is_the_rounded_float32_output(name, opts):
+    """VS_OUT_BF16: O in bf16 equals, bit for bit, the float32 output rounded
+    to nearest even (the same recurrence, only the epilogue's store differs);
+    lse2 unchanged."""
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.generate(w)
+    a = run_plan(q, k, v, **opts)
+    b = run_plan(q, k, v, out_dtype=torch.bfloat16, **opts)
+    assert b.out.dtype == torch.bfloat16
+    assert torch.equal(a.out.to(torch.bfloat16).view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.lse2.view(torch.int32), b.lse2.view(torch.int32))
