@@ -153,3 +153,20 @@ def test_cube_permutation_argument_errors(lib):
     assert lib.vs_cube_permutation(8, 2, 2, 2, 1, 1, 1, None) == 1
     assert lib.vs_cube_permutation(-1, 2, 2, 2, 1, 1, 1, buf) == 1
     assert lib.vs_cube_permutation(0, 2, 2, 2, 1, 1, 1, None) == 0
+
+
+def test_size_limits_are_rejected_before_any_launch(lib):
+    """Sizes past what the kernels address (32-bit per-head buffer ranges,
+    65535 grid rows) return VS_ERR_UNSUPPORTED from the host checks."""
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.vs_fp8_attn_fwd
+    # S = 2^24 at D = 128: one head's codes span 2^31 bytes
+    assert f(fake, fake, fake, fake, fake, fake, None, 0, None, 1, 1 << 24, 1, 128, 0,
+             fake, fake, None) == 2
+    assert f(fake, fake, fake, fake, fake, fake, None, 0, None, 1, (1 << 24) - 128, 1, 128, 4,
+             None, fake, None) == 1            # just below: argument checks run (out NULL)
+    q = lib.vs_quantize_residual
+    assert q(fake, fake, fake, 0, 65536, 300, 2, 128, 0.1, None, None, 0,
+             fake, fake, fake, fake, fake, fake, None, None) == 2
+    assert q(fake, fake, fake, 0, 1, 300, 65536, 128, 0.1, None, None, 0,
+             fake, fake, fake, fake, fake, fake, None, None) == 2
