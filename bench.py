@@ -50,7 +50,7 @@ def _traffic(workload, expcast, v_format="e4m3"):
         return None
 
 
-def _cpu_baseline(w, q, k, v, rows_n):
+def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3"):
     """Time the oracle on one head: quantization of that head's full Q/K/V plus
     the tiled FP8 recurrence for ``rows_n`` evenly spaced query rows over the
     whole K/V context.  Throughput counted as 4 * rows * S * D flops."""
@@ -65,13 +65,15 @@ def _cpu_baseline(w, q, k, v, rows_n):
     rows = pipeline.sample_rows(w.S, rows_n)
     t0 = time.perf_counter()
     pipeline.smoothed_attention_head(qh, kh, vh, rows=rows, kmeans_kt=w.kmeans,
-                                     expcast=w.expcast)
+                                     expcast=expcast, qk_hadamard=qk_hadamard,
+                                     v_format=v_format)
     dt = time.perf_counter() - t0
     flops = 4.0 * len(rows) * w.S * w.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"head 0 of {w.name} (S={w.S}, D={w.D}): full-head statistics and "
-                      f"E4M3 quantizers{' and k-means' if w.kmeans else ''}, then the "
+                      f"quantizers (V {v_format}{', QK Hadamard' if qk_hadamard else ''})"
+                      f"{' and k-means' if w.kmeans else ''}, then the "
                       f"tiled recurrence for {len(rows)} query rows over all {w.S} keys; "
                       f"{dt:.1f} s wall; flops counted 4*rows*S*D"}
 
@@ -196,7 +198,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = _cpu_baseline(w, q, k, v, args.cpu_rows)
+        line["cpu_baseline"] = _cpu_baseline(w, q, k, v, args.cpu_rows, expcast,
+                                             args.qk_hadamard, args.v_format)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
