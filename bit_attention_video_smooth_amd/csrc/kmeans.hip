@@ -426,22 +426,39 @@ __global__ __launch_bounds__(256) void km_hist_kernel(const int32_t* __restrict_
 
 // counts -> start offsets, in place: offset(c, j) = sum_{j' < j} total(j') +
 // sum_{c' < c} count(c', j).
+// Exclusive offsets of the counting sort: chunk[c][j] becomes the number of
+// tokens with a smaller label, plus those with label j in chunks before c
+// (integer, so any summation order gives the same result).  The 256 threads
+// split into P = 256 / k parts per label, each over a contiguous range of
+// chunks: range sums, then per label a scan over the parts and the
+// labels before it, then each range written out.
 __global__ __launch_bounds__(256) void km_scan_kernel(int H, int k, int nchunk,
                                                       int32_t* __restrict__ chunk) {
+  __shared__ int32_t part[256];
   __shared__ int32_t tot[256];
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t bh = static_cast<size_t>(b) * H + h;
   int32_t* ch = chunk + bh * nchunk * k;
-  const int jj = threadIdx.x;
+  const int P = 256 / k;                     // parts per label (k <= 256)
+  const int jj = threadIdx.x % k, p = threadIdx.x / k;
+  const bool active = p < P;
+  const int c0 = active ? static_cast<int>(static_cast<long long>(p) * nchunk / P) : 0;
+  const int c1 = active ? static_cast<int>(static_cast<long long>(p + 1) * nchunk / P) : 0;
   int t = 0;
-  if (jj < k)
-    for (int c = 0; c < nchunk; ++c) t += ch[static_cast<size_t>(c) * k + jj];
-  tot[jj] = (jj < k) ? t : 0;
+  for (int c = c0; c < c1; ++c) t += ch[static_cast<size_t>(c) * k + jj];
+  if (active) part[p * k + jj] = t;
   __syncthreads();
-  if (jj < k) {
+  if (threadIdx.x < k) {
+    int s = 0;
+    for (int q = 0; q < P; ++q) s += part[q * k + threadIdx.x];
+    tot[threadIdx.x] = s;
+  }
+  __syncthreads();
+  if (active) {
     int base = 0;
     for (int i = 0; i < jj; ++i) base += tot[i];
-    for (int c = 0; c < nchunk; ++c) {
+    for (int q = 0; q < p; ++q) base += part[q * k + jj];
+    for (int c = c0; c < c1; ++c) {
       const int n = ch[static_cast<size_t>(c) * k + jj];
       ch[static_cast<size_t>(c) * k + jj] = base;
       base += n;
