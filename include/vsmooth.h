@@ -17,11 +17,17 @@
  *   - output O and the log2 softmax normalizer (FastVideo PR #2048, "Test
  *     Results": output plus log2-LSE); inputs [B, S, H, D] (TeleFuser PR #40,
  *     "Smooth Attention Kernel Accuracy": live shape (1, 32626, 56, 128)).
+ *   - options of the fused prologue and of the 4-bit path (VC-Attention
+ *     summary, Key Contribution 3 and Main Findings): the gather by the
+ *     permutation inside the quantizers, a static space-time cube grouping,
+ *     a QK Hadamard rotation, and the V residual as MXFP4.
  *
  * Conventions for every entry point
- *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates, frees or keeps device memory; scratch space is
- *     passed in as a workspace whose size a *_workspace_bytes query returns.
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the one
+ *     exception, vs_cube_permutation, is a host function on host memory).
+ *     The library never allocates, frees or keeps device memory; scratch
+ *     space is passed in as a workspace whose size a *_workspace_bytes query
+ *     returns.
  *   - bf16 tensors are passed as raw 16-bit patterns (uint16_t).
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
  *     NULL = the null stream), stateless, and safe to call from several host
