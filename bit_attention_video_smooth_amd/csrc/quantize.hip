@@ -248,11 +248,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 
 // OCP MX FP4 (E2M1) nibble of x: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
 // ties to the even code (mantissa bit 0), saturating at 6, sign kept.
+// Below 1 the codes 0, 1, 2 step by 0.5: rint(2 |x|) (round half to even).
+// From 1 up a code is 2 + 2 e + m for |x| = 2^e (1 + m / 2): the float's
+// bits rounded to one mantissa bit, ties to even (add 2^21 - 1 plus the
+// kept bit, carry into the exponent), then exponent and bit read together.
 __device__ __forceinline__ uint32_t fp4_code(float x) {
   const float m = __builtin_fabsf(x);
-  const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
-                     (m >= 3.5f) + (m > 5.0f);
-  return c | (__float_as_uint(x) >> 31 << 3);
+  const uint32_t b = __float_as_uint(m);
+  const uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;
+  const uint32_t hi = min(r - 252u, 7u);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_rintf(2.0f * m));
+  return (m < 1.0f ? lo : hi) | (__float_as_uint(x) >> 31 << 3);
 }
 
 // Smallest e >= -127 with amax <= 6 * 2^e (0 when amax == 0).
