@@ -173,8 +173,9 @@ def _bf16(x):
     return x.to(torch.bfloat16)
 
 
+@pytest.mark.parametrize("v_format", ["e4m3", "mxfp4"])
 @pytest.mark.parametrize("case", ["max_above_64", "max_below_minus_64", "expcast_cap"])
-def test_extreme_score_ranges(case):
+def test_extreme_score_ranges(case, v_format):
     """Rows whose integer running max leaves [-64, 64] (the kernel's fallback
     that forms exp2 of s + 8 - m instead of the scaled pack), and for ExpCast
     rows with |m| >= 2^20 (the per-element cap at 126): same oracle, same bars.
@@ -199,9 +200,10 @@ def test_extreme_score_ranges(case):
     for expcast in (False, True):
         if case == "expcast_cap" and not expcast:
             continue
-        plan = run_plan(q, k, v, smooth=smooth, expcast=expcast)
+        plan = run_plan(q, k, v, smooth=smooth, expcast=expcast, v_format=v_format)
         for h in range(H):
-            ref = oracle_head(q, k, v, 0, h, rows, smooth=smooth, expcast=expcast)
+            ref = oracle_head(q, k, v, 0, h, rows, smooth=smooth, expcast=expcast,
+                              v_format=v_format)
             got = plan_head(plan, 0, h, rows)
             check_intermediates(got, ref, S, label=f"{case} h{h}")
             m_lo = float(np.min(ref["lse2"] - (ref["q_off"] if ref["q_off"] is not None else 0)))
