@@ -78,6 +78,50 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
                       f"{dt:.1f} s wall; flops counted 4*rows*S*D"}
 
 
+def _peaks(dev):
+    """Practical ceilings on this machine next to the published peaks: the
+    vendor library's dense FP8 (E4M3) and bf16 GEMMs (torch._scaled_mm /
+    torch.matmul through hipBLASLt) and a large device-to-device copy, each
+    timed with HIP events after warm-up."""
+    import torch
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    out = {}
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn).t()   # column-major B
+        one = torch.ones((), device=dev)
+        try:
+            t = timed(lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one,
+                                               out_dtype=torch.bfloat16))
+            out[f"fp8_gemm_{n}_tflops"] = round(2.0 * n ** 3 / t / 1e12, 1)
+        except Exception as exc:            # not every build exposes FP8 GEMMs
+            out[f"fp8_gemm_{n}_tflops"] = f"unavailable: {type(exc).__name__}"
+        x = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        y = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        t = timed(lambda: torch.matmul(x, y))
+        out[f"bf16_gemm_{n}_tflops"] = round(2.0 * n ** 3 / t / 1e12, 1)
+        del a, b, x, y
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), n=10)
+    out["copy_4GiB_gbs"] = round(2.0 * src.numel() / t / 1e9, 1)   # read + write
+    out["published"] = {"fp8_dense_tflops": FP8_PEAK_TFLOPS, "bf16_dense_tflops": 2500.0,
+                        "hbm_gbs": HBM_PEAK_GBS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +139,9 @@ def main():
                     help="rotate Q and the centred K by the Hadamard matrix in the quantizers")
     ap.add_argument("--v-format", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="V residual format (mxfp4: E2M1 codes, E8M0 scale per 32 tokens)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the box's practical ceilings (library FP8/bf16 GEMMs, "
+                         "device copy) and print them as one JSON line")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -114,9 +161,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.peaks:
+        print(json.dumps({"peaks": _peaks(dev)}), flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     expcast = w.expcast if args.expcast is None else bool(args.expcast)
-    dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
     q, k, v = workloads.generate(w, device=dev)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
