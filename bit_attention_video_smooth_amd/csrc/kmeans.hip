@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
   const int S32 = round32(S);
   const double sc = ldexp(1.0, -code_exponent(amax[bh]));
   int8_t* const xr = codes + bh * S32 * D;
-  int8_t* const xc = codes_t + bh * S32 * D;
+  int8_t* const xc = codes_t ? codes_t + bh * S32 * D : nullptr;
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int row = r + ROWS * i, tok = j * kBlock + row;
@@ -188,6 +188,8 @@ __global__ __launch_bounds__(256) void km_codes_kernel(const uint16_t* __restric
     *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c) = out[0];
     *reinterpret_cast<uint32_t*>(tile + row * TS + 8 * c + 4) = out[1];
   }
+  // the channel-major copy is only written for the multi-tile assign pass
+  if (codes_t == nullptr) return;
   __syncthreads();
   // channel rows: per 32-token sub-block, D rows of 32 bytes; thread q
   // writes 16 bytes, consecutive q consecutive in memory
@@ -237,8 +239,12 @@ __device__ __forceinline__ uint32_t zero_bytes_to_ones(uint32_t x) {
 //     channel-major codes; the four waves' tiles meet in LDS and one partial
 //     per (chunk, tile) goes to global memory.  Tokens past S have zero codes
 //     there, so their one-hot bytes need no mask.
-template <int D>
-__global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict__ codes,
+//   ONE (k <= 32, a single centroid tile): the sums are taken block by block
+//     right after the labels, from the block's token codes already in
+//     registers, turned into channel rows through a 32 x D byte tile per
+//     wave in LDS; the channel-major copy is then neither written nor read.
+template <int D, bool ONE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 1))) void km_assign_kernel(const int8_t* __restrict__ codes,
                                                         const int8_t* __restrict__ codes_t,
                                                         int S, int H, int k,
                                                         const int8_t* __restrict__ cent,
@@ -253,13 +259,15 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
   __shared__ int32_t scnt[256];
   __shared__ __attribute__((aligned(16))) uint8_t slab[kAsg];
   __shared__ int32_t sred[32 * D];
+  // ONE: per wave, D channel rows of the block's 32 token bytes
+  __shared__ __attribute__((aligned(16))) int8_t stt[ONE ? 4 * D * 32 : 16];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const int nasg = gridDim.x;
   const int S32 = round32(S);
   const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntile = (k + 31) / 32;
+  const int ntile = ONE ? 1 : (k + 31) / 32;
 
   const int4* gc = reinterpret_cast<const int4*>(cent + bh * k * D);
   for (int i = threadIdx.x; i < k * D / 16; i += 256) reinterpret_cast<int4*>(scent)[i] = gc[i];
@@ -282,7 +290,14 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
   const int tb0 = chunk * kAsg + wave * BPW * 32;
   const int nblk = max(0, min(BPW, (S - tb0 + 31) / 32));
   const int8_t* const xr = codes + bh * S32 * D;
-  const int8_t* const xc = codes_t + bh * S32 * D;
+  const int8_t* const xc = ONE ? nullptr : codes_t + bh * S32 * D;
+  int8_t* const tw = stt + (ONE ? wave * D * 32 : 0);
+  // channel row c sits at row c ^ ((c >> 2) & 4): rows 16 apart (the two
+  // lane halves' byte stores) then fall on different banks
+  auto trow = [](int c) { return c ^ ((c >> 2) & 4); };
+  v16i sacc[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) sacc[s] = v16i{};
 
   // ---- labels ----
   // operands of the next block are loaded while this one is processed
@@ -331,6 +346,36 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
         atomicAdd(&scnt[bidx], 1);
       }
     }
+    if constexpr (ONE) {
+      // lane (l32, hh) holds token l32, channels 32 s + 16 hh + e: store them
+      // as channel rows, read back 16 tokens of channel 32 s + l32
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          tw[trow(32 * s + 16 * hh + e) * 32 + l32] =
+              static_cast<int8_t>(static_cast<uint32_t>(x[s][e >> 2]) >> (8 * (e & 3)));
+      // the stores above (and the labels in slab) come from other lanes of
+      // this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint4 lb = *reinterpret_cast<const uint4*>(slab + blk * 32 + 16 * hh);
+      const uint32_t cid = static_cast<uint32_t>(l32) * 0x01010101u;
+      const v4i oh = {static_cast<int>(zero_bytes_to_ones(lb.x ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.y ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.z ^ cid)),
+                      static_cast<int>(zero_bytes_to_ones(lb.w ^ cid))};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4i xt = *reinterpret_cast<const v4i*>(tw + trow(32 * s + l32) * 32 + 16 * hh);
+        sacc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oh, xt, sacc[s], 0, 0, 0);
+      }
+      // the next block's stores must not overtake these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     if (i + 1 < nblk) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) x[s] = xn[s];
@@ -349,11 +394,11 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const int8_t* __restrict
   for (int ct = 0; ct < ntile; ++ct) {
     v16i acc[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc[s] = v16i{};
+    for (int s = 0; s < KS; ++s) acc[s] = ONE ? sacc[s] : v16i{};
     const uint32_t cid = static_cast<uint32_t>(ct * 32 + l32) * 0x01010101u;
     v4i xt[KS];
-    if (nblk > 0) load_xt(0, xt);
-    for (int i = 0; i < nblk; ++i) {
+    if (!ONE && nblk > 0) load_xt(0, xt);
+    for (int i = 0; i < (ONE ? 0 : nblk); ++i) {
       const int blk = wave * BPW + i;
       v4i xtn[KS];
       if (i + 1 < nblk) load_xt(i + 1, xtn);
@@ -531,14 +576,21 @@ void run_kmeans(const uint16_t* k, const uint16_t* v, int B, int S, int H, int k
   const int hfast = nb <= 65535;
   hipLaunchKernelGGL(km_amax_kernel<D>, hfast ? dim3(H, nb, B) : dim3(nb, H, B), dim3(256), 0, st,
                      v, S, H, ws.amax, hfast);
+  // up to 32 clusters the assign pass builds the channel rows itself
+  const bool one = kc <= 32;
   hipLaunchKernelGGL(km_codes_kernel<D>, dim3(nb, H, B), dim3(256), 0, st, v, S, H, ws.amax,
-                     ws.codes, ws.codes_t, 0);
+                     ws.codes, one ? nullptr : ws.codes_t, 0);
   hipLaunchKernelGGL(km_init_kernel<D>, dim3(H, B), dim3(256), 0, st, ws.codes, S, H, kc, ws.cent);
   const int nasg = (S + kAsg - 1) / kAsg;
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(km_assign_kernel<D>, dim3(nasg, H, B), dim3(256),
-                       static_cast<unsigned>((kc + 31) / 32 * 32 * D), st, ws.codes,
-                       ws.codes_t, S, H, kc, ws.cent, labels, ws.psum, ws.pcnt);
+    if (one)
+      hipLaunchKernelGGL((km_assign_kernel<D, true>), dim3(nasg, H, B), dim3(256),
+                         static_cast<unsigned>(32 * D), st, ws.codes, nullptr, S, H, kc, ws.cent,
+                         labels, ws.psum, ws.pcnt);
+    else
+      hipLaunchKernelGGL((km_assign_kernel<D, false>), dim3(nasg, H, B), dim3(256),
+                         static_cast<unsigned>((kc + 31) / 32 * 32 * D), st, ws.codes,
+                         ws.codes_t, S, H, kc, ws.cent, labels, ws.psum, ws.pcnt);
     hipLaunchKernelGGL(km_update_kernel<D>, dim3((kc * D + 255) / 256, H, B), dim3(256), 0, st, H,
                        kc, nasg, ws.cent, ws.psum, ws.pcnt);
   }
