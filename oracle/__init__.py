@@ -16,8 +16,6 @@ kmeans     integer Lloyd k-means on V, stable label sort, joint K/V gather.
 grouping   the static spatiotemporal-cube permutation of a video token grid.
 attention  FP64 dense attention, the tiled online-softmax recurrence with the
            rank-one V-mean restore, E4M3 / ExpCast-FP8 probability casts.
-matrix_core  E4M3 dot products in the arithmetic of the FP8 matrix core the
-           kernel uses for QK^T (the precision its P codes are decided in).
 pipeline   the whole hot path chained in the pages' order.
 
 Parity status of every function is stated in its docstring; the only parts

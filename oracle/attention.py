@@ -9,35 +9,49 @@ attention; FastVideo PR #2048, "Test Results", reports the output and the
 log2-LSE).
 
 ``tiled_attention`` walks the keys in 128-token tiles in the FlashAttention
-order that VC-Attention builds on (summary, "Methodology in Plain English"
-and abstract: an online softmax that keeps a running row max and row sum):
-per tile j, with scores s in log2 units,
+order that VC-Attention builds on (summary, abstract and "Methodology in Plain
+English": an online softmax that keeps the running row maximum and the row
+sum, the scores taken after subtracting that maximum).  Per tile j, with the
+scores s in log2 units:
 
-    m'   = max(m, ceil(max_t s_t))           running max, once per tile
-    p_t  = 2^(s_t - m')                      FP32 exponential
+    s_t  = (Q~ . K~_t) s_Q s_K,j c       exact dot product of the E4M3 operands
+    m'   = max(m, max_t s_t)             running row maximum, once per tile
+    p_t  = 2^(s_t - m')                  the FP32 exponential
     P~   = cast of p to E4M3 (see below)
-    l_j  = tile row sum                      the row sum the recurrence keeps
+    l_j  = sum_t p_t                     the row sum the recurrence keeps
     l    = 2^(m - m') l + l_j
     acc  = 2^(m - m') acc + s_V,j (P~ . R~_j) + l_j mu_V,j
     m    = m'
 
 and O = acc / l, lse2 = m + log2 l + qmu.  The last term of ``acc`` is the
 rank-one restore of the block's V mean from the tile row sum (VC-Attention
-summary, Key Contribution 1: "restored inside the existing online-softmax
-recurrence using the row sum the kernel already accumulates").
+summary, Key Contribution 1: the mean is restored inside the online-softmax
+recurrence from the row sum it already accumulates).
 
-Reading (integer running max): any m' no smaller than the row's scores gives
-the same softmax; the recurrence rounds the running max up to an integer, so
-2^(m - m') and the shift 2^(8 - m') of P below are exact powers of two (an
-exponent change for the matrix core's E8M0 operand scales and for the scaled
-FP8 conversion), and the max moves less often.  p_t stays in (2^-1, 1] at the
-row's largest score of the tile where the max is set.
+Readings:
+
+* Scores.  The pages put QK^T on low-bit matrix cores without fixing how the
+  products are added, so the score is the dot product itself: the sum of the
+  exact products of the decoded E4M3 values, times the block scales and the
+  score constant.  Products of two E4M3 values carry at most 8 significant
+  bits and lie between 2^-18 and 2^18, so a float64 sum of 128 of them is
+  exact in any order.  With ``fp32`` the score is then rounded once to
+  float32 (the pages fix FP32 for the softmax that consumes it).
+* Row sum (ExpCast off).  l_j is the sum of the float32 probabilities p
+  before their cast to E4M3: the row sum a FlashAttention recurrence
+  accumulates, which the mean restore reuses.  The restored output is then
+  mu + sum_t P~_t (v_t - mu) / sum_t p_t, so the probability cast's error
+  multiplies the residual V - mu, not V itself.
+* Row sum (ExpCast on).  No float32 p exists, so l_j is the sum of the
+  decoded codes, 2^-8 sum_t decode(code_t): the normalizer of the ExpCast
+  probability vector that Proposition 3.1 bounds (Key Contribution 4).
+  Either way the rank-one term and l use the same l_j.
 
 Probability casts (``pcast``):
 
-* ``"e4m3"``: P~ = E4M3(p * 2^8) * 2^-8.  Reading: the pages do not fix P's
-  scale; 2^8 is a power of two (exact), maps p = 1 to 256 (code 0x78) and
-  keeps p >= 2^-14 normal.
+* ``"e4m3"``: P~ = E4M3(p 2^8) 2^-8.  Reading: the pages do not fix P's
+  scale; 2^8 is a power of two (exact), maps p = 1 (the row maximum) to 256
+  (code 0x78) and keeps p >= 2^-14 normal.
 * ``"expcast"``: ExpCast-FP8 (VC-Attention summary, Key Contribution 2 and
   Methodology): the E4M3 byte is an affine function of log2 of its value, so
   the code is formed from the log-domain score by one multiply-add and one
@@ -51,45 +65,32 @@ Probability casts (``pcast``):
   range, K0 = 120 - 8 sigma.  rint rounds half to even.
 * ``"none"``: no cast (P~ = p), for the exactness pins.
 
-Row sum (both casts): l_j is the sum of the tile's probabilities as they
-enter PV, the decoded P~ (for ``"none"`` that is the exact p).  Reading: the
-pages restore the mean "from the row sum the online softmax already
-maintains"; summing the same P~ that multiplies V makes the restore exact for
-the quantized probabilities, P~ (V - mu) + mu sum(P~) = P~ V, so block
-demeaning changes nothing but the residual's quantization error.
+Precision (``fp32=True``): the pages fix the exponential (and K centring) at
+FP32 and the operands at E4M3.  Each quantity that decides a code is a
+float32 value obtained by rounding the exact (float64) result of its formula
+once:
 
-Precision (``fp32=True``): the pages fix the exponential and K centring at
-FP32 and the operands at E4M3; every quantity that decides a code is formed
-in float32 with one rounding per operation, in the order below, so a kernel
-that computes in FP32 takes the same decisions.  With scores S (the dot
-product of the E4M3 codes; exactly, rounded to float32, or, with
-``qk_codes``, in the FP8 matrix core's arithmetic, ``matrix_core``):
+    s_t   = f32(S_t * f32(f32(s_Q s_K,j) c))      S_t the exact dot product
+    m'    = max(m, max_t s_t)                     (float32 values)
+    e4m3:    p8_t = f32(2^(s_t - m' + 8)),  P~ code = E4M3(p8_t),
+             l_j = 2^-8 sum_t p8_t
+    expcast: t_t = f32(8 (s_t - m') + f32(K0)),   code = rint(t_t) ...
 
-    c_j  = f32(f32(s_Q s_K,j) * c)   (the pipeline folds c into Q and passes
-                                       c = 1: c_j is then the exact product of
-                                       two power-of-two block scales)
-    s_t  = f32(S_t c_j)
-    m'   = max(m, ceil(max_t s_t))
-    e4m3:    p8_t = f32(2^(s_t + 8 - m')),  P~ code = E4M3(p8_t)
-             (2^(8 - m') is a power of two: the same value as
-             f32(2^s_t) 2^(8 - m'), which is how the kernel forms it)
-    expcast: t_t = f32(8 s_t + f32(K0 - 8 m'))
-    row sum: sum of P~ (with ``qk_codes``, in the matrix core's arithmetic:
-    the tile's P codes in the PV k order against an all-ones operand)
-    accumulation of l and acc: float64.
-
-With ``fp32=False`` everything is float64 and exp2 is exact to float64.
+and l, acc and the rescale factors are float64.  With ``fp32=False``
+everything is float64 and K0 is exact.
 
 Pinned by tests/test_oracle_attention.py: brute-force dense attention on
 tiny shapes (S in {1, 7, 128, 129, 300}, D in {64, 128}) with no cast; the
 K-centring invariance; the V-mean restore identity (block and sequence mean);
-joint K/V permutation invariance; constant-V and equal-score cases with the
-E4M3 cast; the ExpCast total-variation bound of Proposition 3.1 (3.64% plus
-the underflow tail) and its two-point extremal row.
+joint K/V permutation invariance; the exactness of the float64 score; the
+row maximum's code 0x78; lse2 independent of the E4M3 cast; constant-V and
+equal-score cases with the cast; the cast's error bound against the residual;
+the ExpCast total-variation bound of Proposition 3.1 (3.64% plus the
+underflow tail) and its two-point extremal row.
 """
 import numpy as np
 
-from . import e4m3, matrix_core
+from . import e4m3
 
 BLOCK = 128
 
@@ -134,7 +135,7 @@ def _f32(x):
 
 def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
                     v_mean=None, vmean_mode="none", q_off=None, pcast="e4m3",
-                    fp32=True, block=BLOCK, return_trace=False, qk_codes=None):
+                    fp32=True, block=BLOCK, return_trace=False):
     """One head, R query rows, the recurrence of the module docstring.
 
     q_hat   [R, D]   query rows (decoded E4M3 codes, or raw values)
@@ -147,11 +148,8 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
     c       score constant softmax_scale * log2 e (float32 when fp32)
     v_mean  [nb, D] (vmean_mode "block") or [D] ("seq") or None ("none")
     q_off   [R] log2 offset added to lse2 (qmu), or None
-    qk_codes (q_codes [R, D], k_codes [>=S, D]) E4M3 bytes: when given, the
-            raw scores are formed in the FP8 matrix core's arithmetic
-            (``matrix_core.mfma_fp8_dot``) instead of exactly
     Returns (O [R, D] float64, lse2 [R] float64) and, with return_trace, a
-    dict of per-tile P codes (e4m3/expcast) and row sums for diagnostics.
+    dict of per-tile P codes (e4m3/expcast), row sums and running maxima.
     """
     q_hat = np.asarray(q_hat, dtype=np.float64)
     k_hat = np.asarray(k_hat, dtype=np.float64)
@@ -161,31 +159,27 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
     rnd = _f32 if fp32 else (lambda x: np.asarray(x, dtype=np.float64))
     c = float(c)
     q_scale = np.broadcast_to(np.asarray(q_scale, dtype=np.float64), (R,))
+    k0 = float(K0_F32) if fp32 else K0
 
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, D))
-    trace = {"codes": [], "ell": []} if return_trace else None
+    trace = {"codes": [], "ell": [], "m": []} if return_trace else None
     for j in range(nb):
         lo, hi = j * block, min(S, (j + 1) * block)
         n = hi - lo
         kb = k_hat[lo:lo + block]
         vb = v_hat[lo:lo + block]
-        if qk_codes is not None:
-            S_raw = matrix_core.mfma_fp8_dot_c(qk_codes[0], qk_codes[1][lo:hi])
-        else:
-            S_raw = rnd(q_hat @ kb[:n].T)                   # [R, n]
         cj = rnd(rnd(q_scale * float(k_scale[j])) * c)      # [R]
-        s = rnd(S_raw * cj[:, None])
-        m_new = np.maximum(m, np.ceil(s.max(axis=1)))
+        s = rnd((q_hat @ kb[:n].T) * cj[:, None])           # [R, n]
+        m_new = np.maximum(m, s.max(axis=1))
         if pcast == "expcast":
-            k0 = float(K0_F32) if fp32 else K0
-            bias = rnd(k0 - 8.0 * m_new)
-            t = rnd(8.0 * s + bias[:, None])
+            t = rnd(8.0 * (s - m_new[:, None]) + k0)
             codes = expcast_codes(t)
             p_tilde = e4m3.decode(codes) * 2.0 ** -8
+            ell = p_tilde.sum(axis=1)
         else:
-            p8 = rnd(np.exp2(s + (8.0 - m_new)[:, None]))
+            p8 = rnd(np.exp2(s - m_new[:, None] + 8.0))
             if pcast == "e4m3":
                 codes = e4m3.encode(p8)
                 p_tilde = e4m3.decode(codes) * 2.0 ** -8
@@ -194,10 +188,7 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
                 p_tilde = p8 * 2.0 ** -8
             else:
                 raise ValueError(pcast)
-        if codes is not None and qk_codes is not None:
-            ell = matrix_core.row_sum_pv_order(codes) * 2.0 ** -8
-        else:
-            ell = p_tilde.sum(axis=1)
+            ell = p8.sum(axis=1) * 2.0 ** -8
         alpha = np.exp2(m - m_new)          # 0 on the first tile (m = -inf)
         l = alpha * l + ell
         acc = alpha[:, None] * acc + float(v_scale[j]) * (p_tilde @ vb[:n])
@@ -207,6 +198,7 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
         if return_trace:
             trace["codes"].append(codes)
             trace["ell"].append(ell)
+            trace["m"].append(m.copy())
     out = acc / l[:, None]
     if vmean_mode == "seq":
         out = out + np.asarray(v_mean, dtype=np.float64)[None, :]
@@ -216,6 +208,11 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
     if return_trace:
         return out, lse2, trace
     return out, lse2
+
+
+def p_codes_row_major(trace, S):
+    """The traced P codes of every tile concatenated in key order: [R, S]."""
+    return np.concatenate([c for c in trace["codes"]], axis=1)[:, :S]
 
 
 def total_variation(p, q) -> np.ndarray:

@@ -38,7 +38,7 @@ def default_scale(D: int) -> np.float32:
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
                             qk_hadamard=False, v_format="e4m3", expcast=False, pcast=None,
-                            fp32=True, scores="mfma"):
+                            fp32=True):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
@@ -49,8 +49,6 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     v_format: "e4m3" (per-block power-of-two scale) or "mxfp4" (E2M1 codes
     with an E8M0 scale per 32 tokens and channel, ``fp4``).  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
-    scores: "mfma" forms QK^T in the FP8 matrix core's arithmetic (the
-    precision in which the kernel decides every P code), "exact" in float64.
     Returns a dict with O, lse2 and every intermediate the GPU path also
     produces.
     """
@@ -126,7 +124,7 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
         e4m3.decode(k_codes), k_scale, v_hat, v_hat_scale, S, 1.0,
         v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
-        fp32=fp32, qk_codes=(q_codes[rows], k_codes) if scores == "mfma" else None)
+        fp32=fp32)
     out["O"], out["lse2"] = o, lse2
     return out
 

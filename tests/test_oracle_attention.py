@@ -143,10 +143,10 @@ def test_constant_v_is_returned_exactly_with_block_mean_restore():
 
 
 def test_equal_scores_give_the_mean_of_dequantized_v():
-    """All keys identical: every p of a row is the same power 2^(s - m'), so
-    every code of the row is the same and O is the plain average of the
-    dequantized V rows; lse2 = m' + log2(S P~) with P~ = E4M3(2^(s+8-m'))/2^8,
-    within half an E4M3 step of s + log2 S."""
+    """All keys identical: every score of a row equals the row maximum, so
+    every p is exactly 1, every code is 0x78, O is the plain average of the
+    dequantized V rows, and lse2 = s + log2 S exactly (the row sum adds the
+    float32 p, here all 1)."""
     rng = np.random.default_rng(5)
     S, D = 300, 64
     q = rng.standard_normal((S, D)).astype(np.float32)
@@ -156,27 +156,110 @@ def test_equal_scores_give_the_mean_of_dequantized_v():
     rows = np.arange(0, S, 13)
     o, lse2, tr = attention.tiled_attention(e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes), ks,
                                             e4m3.decode(vcodes), vs, S, c, return_trace=True)
-    srow = np.array([float(np.float32(np.float32(e4m3.decode(qc[i]) @ e4m3.decode(kcodes[0])) *
-                                      np.float32(np.float32(qs[i // 128] * ks[0]) * c))) for i in rows])
-    mrow = np.ceil(srow)
-    code = e4m3.encode(np.exp2(srow + 8.0 - mrow).astype(np.float32))
     for codes in tr["codes"]:
-        assert np.all(codes == code[:, None])
+        assert np.all(codes == 0x78)
+    srow = np.array([float(np.float32(sum(float(a) * float(b) for a, b in
+                                          zip(e4m3.decode(qc[i]), e4m3.decode(kcodes[0])))
+                                      * float(qs[i // 128]) * float(ks[0]))) for i in rows])
     deq = smoothing.dequantize_blocks(vcodes, vs, S)
-    # the P~ of a row are all equal, and l sums the P~
     np.testing.assert_allclose(o, np.repeat(deq.mean(0)[None], len(rows), 0), rtol=1e-14, atol=0)
-    expect = mrow + np.log2(S * e4m3.decode(code) / 256.0)
-    np.testing.assert_allclose(lse2, expect, rtol=0, atol=1e-12)
-    assert np.all(np.abs(lse2 - (srow + math.log2(S))) <= math.log2(1 + 2.0 ** -4) + 1e-12)
+    np.testing.assert_allclose(lse2, srow + math.log2(S), rtol=0, atol=1e-12)
 
 
-def test_e4m3_p_cast_error_is_within_half_a_step():
+def test_score_is_the_exact_dot_product():
+    """The recurrence's float64 score of decoded E4M3 operands equals the
+    rational sum of the products (Fraction arithmetic), over codes spanning
+    the whole E4M3 range, subnormals included; with fp32 it is that value
+    rounded once to float32."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    D = 128
+    codes = np.arange(256)
+    finite = codes[~np.isnan(e4m3.DECODE)]
+    qc = rng.choice(finite, size=(4, D)).astype(np.uint8)
+    kc = rng.choice(finite, size=(128, D)).astype(np.uint8)
+    qv, kv = e4m3.decode(qc), e4m3.decode(kc)
+    _, _, tr = attention.tiled_attention(qv, 1.0, kv, np.ones(1), np.zeros((128, 1)), np.ones(1),
+                                         128, 1.0, pcast="none", fp32=False, return_trace=True)
+    exact = np.array([[float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qv[i], kv[t])))
+                       for t in range(128)] for i in range(4)])
+    got = qv @ kv.T
+    assert np.array_equal(got, exact)
+    # the traced row maximum is the maximum of those exact scores
+    np.testing.assert_array_equal(tr["m"][0], exact.max(axis=1))
+    _, _, tr32 = attention.tiled_attention(qv, 1.0, kv, np.ones(1), np.zeros((128, 1)), np.ones(1),
+                                           128, 1.0, pcast="none", fp32=True, return_trace=True)
+    np.testing.assert_array_equal(tr32["m"][0], exact.max(axis=1).astype(np.float32))
+
+
+def test_row_maximum_gets_code_0x78():
+    """The running maximum is the row maximum itself: in the tile holding a
+    row's largest score that key has p = 1 exactly, i.e. E4M3(2^8) = 0x78,
+    and no code of the row exceeds 0x78."""
+    rng = np.random.default_rng(12)
+    S, D = 700, 64
+    q = rng.standard_normal((S, D)).astype(np.float32) * 2
+    k = rng.standard_normal((S, D)).astype(np.float32)
+    v = rng.standard_normal((S, D)).astype(np.float32)
+    c, qc, qs, kcodes, ks, vcodes, vs, bm = _quantized_case(rng, S, D, q, k, v)
+    rows = np.arange(0, S, 7)
+    _, _, tr = attention.tiled_attention(e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes), ks,
+                                         e4m3.decode(vcodes), vs, S, c, v_mean=bm,
+                                         vmean_mode="block", return_trace=True)
+    codes = attention.p_codes_row_major(tr, S)
+    qd = e4m3.decode(qc[rows]) * qs[rows // 128, None].astype(np.float64)
+    sc = qd @ smoothing.dequantize_blocks(kcodes, ks, S).T
+    arg = sc.argmax(axis=1)
+    assert np.all(codes[np.arange(len(rows)), arg] == 0x78)
+    assert codes.max() == 0x78
+
+
+def test_lse2_does_not_depend_on_the_e4m3_cast():
+    """The row sum adds the float32 p before the cast (ExpCast off), so the
+    lse2 with the E4M3 cast equals that with no cast bit for bit, while O
+    differs."""
+    rng = np.random.default_rng(13)
+    S, D = 500, 64
+    q = rng.standard_normal((S, D)).astype(np.float32) * 2
+    k = rng.standard_normal((S, D)).astype(np.float32)
+    v = rng.standard_normal((S, D)).astype(np.float32)
+    c, qc, qs, kcodes, ks, vcodes, vs, bm = _quantized_case(rng, S, D, q, k, v)
+    rows = np.arange(0, S, 5)
+    args = (e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes), ks, e4m3.decode(vcodes),
+            vs, S, c)
+    o1, l1 = attention.tiled_attention(*args, v_mean=bm, vmean_mode="block", pcast="e4m3")
+    o0, l0 = attention.tiled_attention(*args, v_mean=bm, vmean_mode="block", pcast="none")
+    np.testing.assert_array_equal(l1, l0)
+    assert np.max(np.abs(o1 - o0)) > 1e-4
+
+
+@pytest.mark.parametrize("pcast", ["e4m3", "expcast"])
+def test_mean_restore_follows_a_shift_of_the_block_means(pcast):
+    """The rank-one term and l take the same tile row sum, so shifting every
+    block mean by a vector u (residuals unchanged) shifts O by exactly u,
+    whatever the probability cast."""
+    rng = np.random.default_rng(14)
+    S, D = 600, 32
+    q = rng.standard_normal((S, D)).astype(np.float32) * 2
+    k = rng.standard_normal((S, D)).astype(np.float32)
+    v = rng.standard_normal((S, D)).astype(np.float32) + 3.0
+    c, qc, qs, kcodes, ks, vcodes, vs, bm = _quantized_case(rng, S, D, q, k, v)
+    rows = np.arange(0, S, 9)
+    args = (e4m3.decode(qc[rows]), qs[rows // 128], e4m3.decode(kcodes), ks, e4m3.decode(vcodes),
+            vs, S, c)
+    u = rng.standard_normal(D) * 5
+    o1, _ = attention.tiled_attention(*args, v_mean=bm, vmean_mode="block", pcast=pcast)
+    o2, _ = attention.tiled_attention(*args, v_mean=bm + u[None, :], vmean_mode="block",
+                                      pcast=pcast)
+    np.testing.assert_allclose(o2 - o1, np.repeat(u[None], len(rows), 0), rtol=0, atol=1e-12)
+
+
+def test_e4m3_p_cast_error_is_bounded_by_the_values():
     """With exact operands, the E4M3 P cast (2^8 scale) changes each p by at
-    most 2^-4 of itself (p >= 2^-14), so the normalized weights P~/sum(P~)
-    are within total variation 2^-4 (plus the mass below the normal range,
-    at most 2^-18 per key against a row sum of at least 1/2, the row max
-    having p in (1/2, 1]) of p/sum(p), and each output channel within that
-    share of its range."""
+    most 2^-4 of itself (p >= 2^-14; below that by at most 2^-18), and O is
+    sum_t P~_t v_t / sum_t p_t (the row sum adds the p before the cast, and
+    the row maximum has p = 1), so each output channel moves by at most
+    (2^-4 + S 2^-18) max_t |v_t|."""
     rng = np.random.default_rng(6)
     S, D = 700, 64
     q = rng.standard_normal((20, D)) * 2
@@ -191,8 +274,8 @@ def test_e4m3_p_cast_error_is_within_half_a_step():
                                       np.pad(v, ((0, pad), (0, 0))), np.ones(nb), S, c,
                                       pcast="e4m3", fp32=False)
     err = np.abs(oc - od)
-    diam = v.max(axis=0) - v.min(axis=0)
-    assert np.all(err <= (2.0 ** -4 + S * 2.0 ** -17) * diam[None, :])
+    vmax = np.abs(v).max(axis=0)
+    assert np.all(err <= (2.0 ** -4 + S * 2.0 ** -18) * vmax[None, :])
     assert np.all(err.max(axis=1) > 0)          # the cast really happened
 
 
@@ -241,9 +324,9 @@ def test_expcast_tv_bound_on_random_rows():
         assert tv <= attention.EXPCAST_TV_BOUND + tail + 1e-12
         worst = max(worst, tv - tail)
         # per element: log2 error within sigma + 1/16 where the code is normal
-        # (codes are relative to the integer running max)
+        # (codes are relative to the row maximum)
         nz = codes != 0
-        err = np.log2(e4m3.decode(codes[nz]) / 256.0) - (s[nz] - np.ceil(s.max()))
+        err = np.log2(e4m3.decode(codes[nz]) / 256.0) - (s[nz] - s.max())
         assert np.all(np.abs(err) <= attention.EXPCAST_LOG2_ERR + 1e-12)
     assert worst > 0.005
 
