@@ -12,6 +12,7 @@ VS_EXPCAST = 1
 VS_QK_HADAMARD = 1
 VS_V_MXFP4 = 2
 VS_OUT_BF16 = 4
+VS_BF16_MMA = 8
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -34,6 +35,8 @@ PROTOTYPES = {
                                      _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_fp8_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,
                              _P, _P, _P]),
+    "vs_fp8_attn_fwd_pcodes": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,
+                                    _P, _P, _P, _I, _P]),
     "vs_cube_permutation": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "vs_kmeans_workspace_bytes": (_I, [_I, _I, _I, _I, _I, _PZ]),
     "vs_kmeans_permute": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),

@@ -15,12 +15,12 @@ import math
 import torch
 
 from . import _abi
-from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_BF16_MMA, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
            "vs_quantize_residual_perm", "vs_quantize_residual_ex",
-           "vs_fp8_attn_fwd", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
+           "vs_fp8_attn_fwd", "vs_fp8_attn_fwd_pcodes", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
            "vs_cube_permutation",
            "vs_version", "Plan", "attention"]
 
@@ -108,6 +108,17 @@ def vs_fp8_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q
                                  _p(out), _p(lse2), _stream(dev)), "vs_fp8_attn_fwd")
 
 
+def vs_fp8_attn_fwd_pcodes(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu,
+                           shape, flags, out, lse2, p_codes, row_stride):
+    B, S, H, D = shape
+    dev = _dev(q8, k8, v8)
+    check(load().vs_fp8_attn_fwd_pcodes(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v8),
+                                        _p(v_scale), _p(v_mean), vmean_mode, _p(q_mu), B, S, H,
+                                        D, int(flags), _p(out), _p(lse2), _p(p_codes),
+                                        int(row_stride), _stream(dev)),
+          "vs_fp8_attn_fwd_pcodes")
+
+
 def vs_cube_permutation(S, grid, cube):
     """Host call: int32 CPU tensor [S], the static cube grouping of a
     T x Hg x W token grid (include/vsmooth.h)."""
@@ -149,12 +160,17 @@ class Plan:
     quantization (VS_QK_HADAMARD); v_format: "e4m3" or "mxfp4" (the V
     residual as E2M1 codes with an E8M0 scale per 32 tokens and channel,
     VS_V_MXFP4: v8 is then u8 [B,H,nb,D,64] and v_scale u8 [B,H,nb,D,4]);
-    out_dtype: torch.float32 or torch.bfloat16 (VS_OUT_BF16).
+    out_dtype: torch.float32 or torch.bfloat16 (VS_OUT_BF16); mma: "fp8"
+    (QK^T and PV on the FP8 matrix core from the E4M3 / E2M1 codes) or
+    "bf16" (VS_BF16_MMA: the quantizers write the same quantized values
+    times their scales as bf16 -- q8, k8 bf16 [B,H,S_pad,D], v8 bf16
+    [B,H,nb,D,128] in the bf16 PV's token order -- and both products run on
+    the bf16 matrix core, float32-accurate).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
                  kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False,
-                 v_format="e4m3", out_dtype=torch.float32):
+                 v_format="e4m3", out_dtype=torch.float32, mma="fp8"):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -168,19 +184,28 @@ class Plan:
         v4 = VS_V_MXFP4 if v_format == "mxfp4" else 0
         if out_dtype not in (torch.float32, torch.bfloat16):
             raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
-        self.flags = ((VS_EXPCAST if expcast else 0) | v4 |
+        if mma not in ("fp8", "bf16"):
+            raise ValueError(f"unknown mma {mma!r}")
+        self.mma = mma
+        b16 = VS_BF16_MMA if mma == "bf16" else 0
+        # with the bf16 products attention takes V as bf16 values, whatever
+        # format quantized them
+        self.flags = ((VS_EXPCAST if expcast else 0) | (0 if b16 else v4) | b16 |
                       (VS_OUT_BF16 if out_dtype == torch.bfloat16 else 0))
-        self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4
+        self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4 | b16
         nb = (S + 127) // 128
         dev = self.device
         f32, u8, i32 = torch.float32, torch.uint8, torch.int32
         e = lambda *s, dtype=f32: torch.empty(*s, dtype=dtype, device=dev)  # noqa: E731
-        self.q8, self.k8 = e(B, H, nb * 128, D, dtype=u8), e(B, H, nb * 128, D, dtype=u8)
+        qkt = torch.bfloat16 if b16 else u8
+        self.q8, self.k8 = e(B, H, nb * 128, D, dtype=qkt), e(B, H, nb * 128, D, dtype=qkt)
         self.q_scale, self.k_scale = e(B, H, nb), e(B, H, nb)
         if v4:
             self.v8, self.v_scale = e(B, H, nb, D, 64, dtype=u8), e(B, H, nb, D, 4, dtype=u8)
         else:
             self.v8, self.v_scale = e(B, H, nb, D, 128, dtype=u8), e(B, H, nb)
+        if b16:
+            self.v8 = e(B, H, nb, D, 128, dtype=torch.bfloat16)
         self.out, self.lse2 = e(B, S, H, D, dtype=out_dtype), e(B, H, S)
         self.k_mean = self.q_mu = self.v_mean = self.stats_ws = None
         if smooth:
@@ -254,6 +279,19 @@ class Plan:
         vs_fp8_attn_fwd(self.q8, self.q_scale, self.k8, self.k_scale, self.v8, self.v_scale,
                         self.v_mean, self.vmean_mode, self.q_mu, self.shape, self.flags,
                         self.out, self.lse2)
+
+    def attn_pcodes(self, row_stride):
+        """The attention call again, also returning the E4M3 probability codes
+        of every row_stride-th query row: u8 [B, H, ceil(S/stride), S_pad], the
+        codes of key t at column t (vs_fp8_attn_fwd_pcodes, a diagnostic)."""
+        B, S, H, D = self.shape
+        nb = (S + 127) // 128
+        n = (S + row_stride - 1) // row_stride
+        codes = torch.zeros(B, H, n, nb * 128, dtype=torch.uint8, device=self.device)
+        vs_fp8_attn_fwd_pcodes(self.q8, self.q_scale, self.k8, self.k_scale, self.v8,
+                               self.v_scale, self.v_mean, self.vmean_mode, self.q_mu, self.shape,
+                               self.flags, self.out, self.lse2, codes, row_stride)
+        return codes
 
 
 def attention(q, k, v, **kw):

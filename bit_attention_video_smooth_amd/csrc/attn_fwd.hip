@@ -3,9 +3,10 @@
 //
 // Method (VC-Attention summary, Key Contributions 1-2 and "Methodology in
 // Plain English"; abstract): QK^T and PV run on the low-bit matrix cores,
-// the online softmax between them keeps a running row max and row sum, and
-// each block's V mean is added back as a rank-one term from the tile row
-// sum.  Output O and log2-LSE as in FastVideo PR #2048 ("Test Results").
+// the online softmax between them keeps the running row maximum and the row
+// sum of the probabilities, and each block's V mean is added back as a
+// rank-one term from that tile row sum.  Output O and log2-LSE as in
+// FastVideo PR #2048 ("Test Results").
 //
 // gfx950 mapping
 //   1-D grid over (batch, head, pair of 128-query blocks), ordered so that
@@ -17,32 +18,36 @@
 //   groups run a ping-pong one phase apart, separated by workgroup barriers:
 //   while one wave issues its matrix-core phase, the other wave on the SIMD
 //   runs its vector phase.
-//     M(j): S^T = K_j Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (A = 32 keys x
-//       64 channels from LDS, B = the wave's 32 queries, held in registers
-//       for the whole loop; a lane owns one query (lane % 32) and 16 keys per
-//       32-key sub-tile; the power-of-two K and Q block scales are the E8M0
-//       operand scales, and Q carries softmax_scale * log2 e, so the product
-//       is the score in log2 units), then for tile j - 1: the row sum of its E4M3
-//       probabilities (P codes as the B operand of two 16x16x128 products
-//       against a 0/1 A operand that keeps a lane's two queries apart), O^T +=
-//       2^e 2^-8 V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (the
-//       power-of-two V block scale and P's 2^8 are E8M0 operand scales, so
-//       the product accumulates straight into acc), and the rank-one restore
-//       acc += mu (x) l as v_mfma_f32_32x32x1_2b_f32 outer products.
-//     V(j): tile max (one cross-half exchange), integer running max, O^T
-//       rescale by an exact power of two (only when some row's max moved),
-//       and P = E4M3(2^s / 2^(m - 8)) -- exp2 of the score and the scaled
-//       FP8 pack, whose power-of-two scale applies the offset -- packed straight into
-//       the B operand of PV: the accumulator layout of two key sub-tiles is
-//       exactly one 64-token k-step of the PV MFMA, given that V is stored in
-//       the matching token order (vs_quantize_residual).
-//   K and V tiles (16 KB each at D = 128) are double-buffered in LDS, shared
-//   by all eight waves, and filled by the first group with buffer_load ...
-//   lds (no staging registers, no per-lane address arithmetic): each lane's
-//   16-byte source is chosen so the LDS image is the XOR-swizzled tile, and
-//   the 128-bit operand reads of 16 consecutive rows hit distinct banks
-//   (gfx950's LDS serves a 128-bit read over 64 banks: rows of 128 B need the
-//   chunk index XORed with (row >> 1) & 7).  The ragged last tile's mask sits
+//     M(j): S^T = K_j Q^T, A = 32 keys from LDS, B = the wave's 32 queries
+//       held in registers for the whole loop (a lane owns one query, lane %
+//       32, and 16 keys per 32-key sub-tile).  Two forms:
+//         FP8: v_mfma_scale_f32_32x32x64_f8f6f4 on the E4M3 codes, the
+//           power-of-two K and Q block scales as E8M0 operand scales;
+//         bf16 (VS_BF16_MMA): v_mfma_f32_32x32x16_bf16 on the decoded codes
+//           with the block scales folded in (the FP8 matrix core truncates
+//           small products inside each group of 8 to about 13 bits below the
+//           group's largest; the bf16 one keeps float32 accuracy at half
+//           the rate).
+//       Q carries softmax_scale * log2 e, so the product is the score in
+//       log2 units, and the first product of each sub-tile takes as its
+//       accumulator the per-row bias 8 - m (m the running max): the matrix
+//       core returns x = s - m + 8 directly.  Then for tile j - 1:
+//       O^T += 2^e 2^-8 V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 (the
+//       power-of-two V block scale and P's 2^8 are E8M0 operand scales) and
+//       the rank-one restore acc += mu (x) l_tile as
+//       v_mfma_f32_32x32x1_2b_f32 outer products.
+//     V(j): tile max of x (one cross-half exchange); where some row's max
+//       grew (a uniform branch), x, O^T and l are shifted by the growth and
+//       the bias moves; then p8 = 2^x, the E4M3 codes E4M3(p8) packed
+//       straight into the B operand of PV (the accumulator layout of two
+//       key sub-tiles is one 64-token k-step of PV, given V stored in the
+//       matching token order), and the tile row sum of the float32 p.
+//   K and V tiles are double-buffered in LDS, shared by all eight waves, and
+//   filled by the first group with buffer_load ... lds (no staging
+//   registers, no per-lane address arithmetic): each lane's 16-byte source
+//   is chosen so the LDS image is the XOR-swizzled tile, and the 128-bit
+//   operand reads of 16 consecutive rows hit distinct banks (gfx950's LDS
+//   serves a 128-bit read over 64 banks).  The ragged last tile's mask sits
 //   behind a uniform branch.
 #include <float.h>
 
@@ -55,8 +60,8 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr float kExpcastK0 = 119.66015f;   // 120 - 4 (log2(1.5) - 1/2)
 
-typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   v8i r;
@@ -65,9 +70,10 @@ __device__ __forceinline__ v8i make_v8i(const uint4& a, const uint4& b) {
   return r;
 }
 
-// 16x16x128 FP8 product without operand scales.
-__device__ __forceinline__ v4f mfma_fp8_16(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ v8bf as_v8bf(const uint4& x) {
+  v8bf r;
+  __builtin_memcpy(&r, &x, 16);
+  return r;
 }
 
 // E8M0 byte of a power-of-two float scale (its biased exponent).
@@ -83,25 +89,42 @@ __device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// XOR swizzle of a row's 16-byte chunk index: rows of 8 chunks (128 B) use
-// (row >> 1) & 7, rows of 4 chunks (64 B) use (row >> 1) & 3.
+// XOR swizzle of a row's 16-byte chunk index, so that 16 lanes reading one
+// chunk column of 16 consecutive rows touch 64 distinct banks: rows of 16
+// chunks (256 B) use row & 15, rows of 8 chunks (128 B) (row >> 1) & 7,
+// rows of 4 chunks (64 B) (row >> 1) & 3.
 template <int ROWCHUNKS>
 __device__ __forceinline__ int row_swz(int row) {
-  return ROWCHUNKS == 8 ? ((row >> 1) & 7) : ((row >> 1) & 3);
+  return ROWCHUNKS == 16 ? (row & 15) : ROWCHUNKS == 8 ? ((row >> 1) & 7) : ((row >> 1) & 3);
 }
 
 // Source chunk, inside one 64-chunk (1 KB) DMA block `blk` of a tile, for the
 // LDS chunk position `lane`: that position holds logical chunk
-// (position ^ swizzle(row)) of its row.  Only the parity of the block index
-// matters for 8-chunk rows (8 rows per block); none for 4-chunk rows.
+// (position ^ swizzle(row)) of its row.  The block index matters modulo 4
+// for 16-chunk rows (4 rows per block), modulo 2 for 8-chunk rows (8 rows
+// per block), not at all for 4-chunk rows.
 template <int ROWCHUNKS>
 __device__ __forceinline__ int dma_src_chunk(int lane, int blk) {
+  if (ROWCHUNKS == 16) {
+    const int row = 4 * blk + (lane >> 4);
+    return (lane & ~15) | ((lane & 15) ^ row_swz<16>(row));
+  }
   if (ROWCHUNKS == 8) {
     const int row = 8 * blk + (lane >> 3);
     return (lane & ~7) | ((lane & 7) ^ row_swz<8>(row));
   }
   const int row = 16 * blk + (lane >> 2);
   return (lane & ~3) | ((lane & 3) ^ row_swz<4>(row));
+}
+
+// a[i] for a runtime i without indexing a private array (which would live
+// in scratch memory): a chain of selects.
+template <int N>
+__device__ __forceinline__ int pick(const int (&a)[N], int i) {
+  int r = a[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = i == k ? a[k] : r;
+  return r;
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -119,59 +142,77 @@ __device__ __forceinline__ void dma16(rsrc_t rs, int voff, int soff, void* dst) 
                                            voff, soff, 0, 0);
 }
 
+// Bytes of one K row in LDS and HBM: D codes, or D bf16 values.
+template <int D, bool BF>
+constexpr int k_row_bytes() { return BF ? 2 * D : D; }
+
 // Uniform values and per-lane constants of one wave.
-template <int D>
+template <int D, bool BF>
 struct Ctx {
+  static constexpr int KRC = k_row_bytes<D, BF>() / 16;   // 16-byte chunks per K row
+  static constexpr int NKS = BF ? D / 16 : D / 64;        // k-steps of the QK product
   rsrc_t krs, vrs, murs, scrs;           // K codes, V codes, V block means, V group scales
   const float* ksc;                      // K block scales of this head
   const float* vsc;                      // V block scales of this head
   int q_e8;                              // E8M0 byte of this query block's scale
   int nb, S, dma_wave, hh, lane;         // dma_wave: 0-3 in the DMA group, else -1
-  int k_src[2], v_src[2];                // DMA source offsets (even / odd 1 KB block)
-  int k_rd[D / 64][2], v_rd[2][2];       // swizzled operand read offsets
+  int k_src[KRC == 16 ? 4 : 2];          // K DMA source offsets (1 KB block mod 4 or 2)
+  int v_src[BF ? 4 : 2];                 // V DMA source offsets
+  int k_rd[NKS][BF ? 1 : 2];             // swizzled K operand read offsets
+  int v_rd[BF ? 8 : 2][BF ? 1 : 2];      // swizzled V operand read offsets
   int v4_rd[2];                          // MXFP4 V: read offset of k-step kk
-  v8i qa[D / 64];                        // this lane's query, B operand of QK
-  v8i ones;                              // E4M3 ones or zeros, A operand of the row sums
+  v8i qa[BF ? 1 : D / 64];             // this lane's query codes, B operand of QK (FP8)
+  v8bf qb[BF ? D / 16 : 1];            // this lane's query as bf16, B operand (bf16)
 };
 
-// Recurrence state of one wave: log2-domain scores s of the current key
-// tile, its E4M3 probabilities pb, the integer running max m, the factor
-// alpha of the last tile (applied to O^T already, to l when that tile's row
-// sum is known), O^T and l.
-template <int D>
+// Recurrence state of one wave: x = s - m + 8 of the current key tile (s
+// the log2-domain score, m the running row max), its E4M3 probabilities pb
+// (as the bf16 values pbf for the bf16 PV), O^T, the bias 8 - m as the first
+// QK product's accumulator, l (the row sum of p8 = 2^8 p = 2^x) and the
+// last tile's row sum for its mean restore.  O^T, l and the row sums are in
+// units of 2^8 p: O = acc / l is unchanged and lse2 = m + log2(l) - 8.
+template <int D, bool BF>
 struct State {
   v16f s[4];
-  v8i pb[2];
+  v8i pb[BF ? 1 : 2];
+  v8bf pbf[BF ? 8 : 1];
   v16f acc[D / 32];
-  float m, alpha, l;
+  v16f bias;
+  float b, l, ell;
   // block scales one tile ahead of their use (scalar loads complete while a
   // whole phase runs): K scale of the next M phase's QK tile, V scale of the
   // next M phase's PV tile
   float ks, vs;
 };
 
-// K of tile j into dst: 16 KB (D = 128) as 1 KB DMA blocks, a quarter per
-// wave of the DMA group.
-template <int D>
-__device__ __forceinline__ void issue_k(const Ctx<D>& c, int j, uint8_t* dst) {
-  constexpr int TB = kBlock * D, NDMA = TB / 16 / 64 / 4;
+// K of tile j into dst (16 KB of codes at D = 128, 32 KB as bf16) as 1 KB
+// DMA blocks, a quarter per wave of the DMA group.
+template <int D, bool BF>
+__device__ __forceinline__ void issue_k(const Ctx<D, BF>& c, int j, uint8_t* dst) {
+  constexpr int TB = kBlock * k_row_bytes<D, BF>(), NDMA = TB / 16 / 64 / 4;
+  constexpr int NSRC = Ctx<D, BF>::KRC == 16 ? 4 : 2;
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int base = (c.dma_wave * NDMA + i) * 1024;
-    dma16(c.krs, c.k_src[i & 1], j * TB + base, dst + base);
+    const int blk = c.dma_wave * NDMA + i;
+    dma16(c.krs, pick(c.k_src, blk % NSRC), j * TB + blk * 1024, dst + blk * 1024);
   }
 }
 
+// Bytes of one V tile: D channel rows of 128 tokens, as E4M3 codes, MXFP4
+// nibbles or bf16 values.
+template <int D, bool BF, bool V4>
+constexpr int v_tile_bytes() { return BF ? kBlock * D * 2 : V4 ? kBlock * D / 2 : kBlock * D; }
+
 // V of tile j (E4M3: 16 KB at D = 128; MXFP4: 8 KB of codes plus the
-// D x 4 group scale bytes), and its block mean.
-template <int D, int VMEAN, bool V4>
-__device__ __forceinline__ void issue_v(const Ctx<D>& c, int j, uint8_t* dst, float* mu_dst,
+// D x 4 group scale bytes; bf16: 32 KB), and its block mean.
+template <int D, bool BF, int VMEAN, bool V4>
+__device__ __forceinline__ void issue_v(const Ctx<D, BF>& c, int j, uint8_t* dst, float* mu_dst,
                                         uint8_t* sc_dst) {
-  constexpr int TB = kBlock * D / (V4 ? 2 : 1), NDMA = TB / 16 / 64 / 4;
+  constexpr int TB = v_tile_bytes<D, BF, V4>(), NDMA = TB / 16 / 64 / 4;
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int base = (c.dma_wave * NDMA + i) * 1024;
-    dma16(c.vrs, c.v_src[i & 1], j * TB + base, dst + base);
+    const int blk = c.dma_wave * NDMA + i;
+    dma16(c.vrs, pick(c.v_src, blk % (BF ? 4 : 2)), j * TB + blk * 1024, dst + blk * 1024);
   }
   if (VMEAN == VS_VMEAN_BLOCK && c.dma_wave == 0 && c.lane < D / 4)
     dma16(c.murs, 16 * c.lane, j * D * 4, mu_dst);
@@ -217,101 +258,103 @@ __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
   return max_with_other_half(mx);
 }
 
-// E4M3 probability codes of 4 scores of one lane (the dword w of sub-tile t
-// of the B operand of PV), |m| <= 64: 2^s is finite and normal down to where
-// its code is 0, and the pack divides it by 2^(m - 8) exactly before
-// rounding to nearest even.
-__device__ __forceinline__ int p_codes4_fast(const v16f& s, int w, float sc) {
-  const float e0 = __builtin_amdgcn_exp2f(s[4 * w + 0]);
-  const float e1 = __builtin_amdgcn_exp2f(s[4 * w + 1]);
-  const float e2 = __builtin_amdgcn_exp2f(s[4 * w + 2]);
-  const float e3 = __builtin_amdgcn_exp2f(s[4 * w + 3]);
+// E4M3 probability codes of 4 elements of one lane (the dword w of sub-tile
+// t of the B operand of PV): p8 = 2^x (x <= 8 up to rounding, so p8 <= 256
+// needs no clamp), rounded to nearest even by the FP8 conversion; the
+// float32 p8 are added to the lane's row-sum part.
+__device__ __forceinline__ int p_codes4(const v16f& x, int w, float& ls) {
+  const float e0 = __builtin_amdgcn_exp2f(x[4 * w + 0]);
+  const float e1 = __builtin_amdgcn_exp2f(x[4 * w + 1]);
+  const float e2 = __builtin_amdgcn_exp2f(x[4 * w + 2]);
+  const float e3 = __builtin_amdgcn_exp2f(x[4 * w + 3]);
+  ls += (e0 + e1) + (e2 + e3);
   // the high half is written next, so the low write may keep any upper
   // bits: reuse e0's register instead of a zeroed one
-  v2s o;
-  __builtin_memcpy(&o, &e0, 4);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, e0, e1, sc, false);
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, e2, e3, sc, true);
-  int pk;
-  __builtin_memcpy(&pk, &o, 4);
-  return pk;
+  uint32_t pk = cvt_pk_e4m3<false>(e0, e1, __float_as_uint(e0));
+  return static_cast<int>(cvt_pk_e4m3<true>(e2, e3, pk));
 }
 
-// The same codes for any m (exp2 of s + 8 - m, rounded to float32 first),
-// or the ExpCast codes.
-template <bool EXPCAST, bool CAP>
-__device__ __forceinline__ int p_codes4(const v16f& s, int w, float bias) {
-  if (!EXPCAST) {
-    const float p0 = __builtin_amdgcn_exp2f(s[4 * w + 0] + bias);
-    const float p1 = __builtin_amdgcn_exp2f(s[4 * w + 1] + bias);
-    const float p2 = __builtin_amdgcn_exp2f(s[4 * w + 2] + bias);
-    const float p3 = __builtin_amdgcn_exp2f(s[4 * w + 3] + bias);
-    // the high half is written next, so the low write may keep any upper
-    // bits: reuse p0's register instead of a zeroed one
-    uint32_t pk = cvt_pk_e4m3<false>(p0, p1, __float_as_uint(p0));
-    return static_cast<int>(cvt_pk_e4m3<true>(p2, p3, pk));
-  }
-  // ExpCast: code = rint(8 (s - m') + K0), capped at 126, codes below 8 -> 0.
-  // v_cvt_pk_u8_f32 rounds half to even and saturates at 0 (so negative
-  // pre-codes and -inf of masked keys give 0) while packing the byte.  The
-  // cap only binds when |m'| is huge (CAP, a uniform slow path); otherwise
-  // every byte is <= 121, so b + 0x78 carries into bit 7 exactly when b >= 8,
-  // and the mask 0x80 - 0x01 = 0x7F keeps those bytes and clears the rest.
+// ExpCast codes of the same 4 elements: code = rint(8 (s - m) + K0) =
+// rint(8 x + K0 - 64), one FMA each; v_cvt_pk_u8_f32 rounds half to even and
+// saturates at 0 (so negative pre-codes and the -inf of masked keys give 0)
+// while packing the byte; x <= 8 keeps every code <= 120, so no cap binds.
+// Codes below 8 become 0: every byte is <= 120, so b + 0x78 carries into bit
+// 7 exactly when b >= 8, and the mask 0x80 - 0x01 = 0x7F keeps those bytes.
+// The decoded codes (hardware E4M3 -> f32, exact) are added to the lane's
+// row-sum part.
+__device__ __forceinline__ int expcast_codes4(const v16f& x, int w, float& ls) {
   uint32_t pk = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float x = __builtin_fmaf(s[4 * w + e], 8.0f, bias);
-    if (CAP) x = __builtin_fminf(x, 126.0f);
-    pk = __builtin_amdgcn_cvt_pk_u8_f32(x, e, pk);
-  }
+  for (int e = 0; e < 4; ++e)
+    pk = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + e], 8.0f, kExpcastK0 - 64.0f), e,
+                                        pk);
   const uint32_t m = (pk + 0x78787878u) & 0x80808080u;
-  return static_cast<int>(pk & (m - (m >> 7)));
+  pk &= m - (m >> 7);
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(pk), false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(pk), true);
+  ls += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+  return static_cast<int>(pk);
 }
 
 // Matrix-core phase M(j) of one wave: S^T of key tile j (if j < nb), then
-// for tile j - 1 (if j >= 1) the row sums of its E4M3 probabilities, PV and
-// the rank-one mean restore, and l's update.
+// for tile j - 1 (if j >= 1) PV and the rank-one mean restore.
 //   kb: K of tile j      vb, mub: V and V mean of tile j - 1
-template <int D, int VMEAN, bool V4>
-__device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D>& st,
+template <int D, bool BF, int VMEAN, bool V4>
+__device__ __forceinline__ void phase_mfma(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
                                            const uint8_t* kb, const uint8_t* vb,
                                            const float* mub, const uint8_t* scb) {
-  constexpr int KD = D / 64, DT = D / 32;
+  constexpr int DT = D / 32, NKS = Ctx<D, BF>::NKS, KRB = k_row_bytes<D, BF>();
   // the matrix-core phase issues first when both waves of the SIMD are ready
   __builtin_amdgcn_s_setprio(1);
   if (j < c.nb) {
-    const int ks_e8 = e8m0_of(st.ks);
-    // sub-tile major is fine here: the products of other waves fill the gap
+    if constexpr (BF) {
+      // k-step major: four independent accumulators in flight
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint8_t* kr = kb + t * 32 * D;
-        const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][1]));
-        st.s[t] = mfma_fp8_scaled(a, c.qa[kd], kd == 0 ? v16f{} : st.s[t], ks_e8, c.q_e8);
-      }
+        for (int t = 0; t < 4; ++t) {
+          const v8bf a = as_v8bf(lds_read16(kb + t * 32 * KRB + c.k_rd[ks][0]));
+          st.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c.qb[ks], ks == 0 ? st.bias : st.s[t],
+                                                            0, 0, 0);
+        }
+    } else {
+      const int ks_e8 = e8m0_of(st.ks);
+#pragma unroll
+      for (int kd = 0; kd < NKS; ++kd)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint8_t* kr = kb + t * 32 * KRB;
+          const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][BF ? 0 : 1]));
+          st.s[t] = mfma_fp8_scaled(a, c.qa[kd], kd == 0 ? st.bias : st.s[t], ks_e8, c.q_e8);
+        }
+    }
   }
   if (j >= 1) {
-    // row sums on the 16x16x128 product, half the cost of a 32x32x64 one.
-    // Read as that shape, the P operand of one PV k-step holds in lane l
-    // column l % 16 and the 32 k values of lane group l / 16; those lanes
-    // carry query l % 32, i.e. column n pairs query n (groups 0 and 2)
-    // with query n + 16 (groups 1 and 3).  A row m of ones over the groups
-    // of parity (m / 4) % 2 only then sums one query, and the output row
-    // of lane l (4 (l / 16) + r) has that parity of l / 16: every lane's
-    // accumulator holds its own query's sum over the tile's 128 keys.
-    v4f rs = mfma_fp8_16(c.ones, st.pb[0], v4f{});
-    rs = mfma_fp8_16(c.ones, st.pb[1], rs);
-    // O^T += 2^e 2^-8 V^T P^T: the E8M0 byte of the V block scale (a normal
-    // power of two: its exponent field) and 2^-8 for P's prescale
+    if constexpr (BF) {
+      // O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: A = 32 channels x 16
+      // tokens of the bf16 V tile (its block scale folded into the values),
+      // B = the 16 tokens' probabilities of the wave's 32 queries (k-step ks
+      // holds sub-tile ks / 2's elements 8 (ks % 2) .. + 7 of every lane,
+      // the token order the quantizer wrote V in); channel tiles innermost,
+      // so DT accumulators are in flight
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const v8bf a = as_v8bf(lds_read16(vb + dt * 32 * 256 + c.v_rd[ks][0]));
+          st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pbf[ks], st.acc[dt], 0, 0, 0);
+        }
+    } else {
+    // O^T += 2^e V^T P^T: the E8M0 byte of the V block scale (a normal
+    // power of two: its exponent field); P is in units of 2^8 p
     const int sv_e8 = (__float_as_int(st.vs) >> 23) & 0xFF;
     // V fragments read one product ahead (the fence keeps each read above
     // the product before it)
     auto vfrag = [&](int i) {
       const uint8_t* vr = vb + (i % DT) * 32 * kBlock;
-      return make_v8i(lds_read16(vr + c.v_rd[i / DT][0]), lds_read16(vr + c.v_rd[i / DT][1]));
+      return make_v8i(lds_read16(vr + c.v_rd[i / DT][0]), lds_read16(vr + c.v_rd[i / DT][BF ? 0 : 1]));
     };
-    if (V4) {
+    if constexpr (V4) {
       // MXFP4 V^T: lane (channel 32 dt + lane % 32, half hh) holds k-step
       // kk's tokens 64 kk + 32 hh .. + 31 in 16 bytes, and passes its own
       // E8M0 group scale (byte 2 kk + hh of its channel's scale word)
@@ -332,7 +375,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
         __builtin_amdgcn_sched_barrier(0);
         const int sa = static_cast<int>((sw[i % DT] >> (16 * (i / DT))) & 0xFF);
         st.acc[i % DT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a, st.pb[i / DT], st.acc[i % DT], 4, 0, 0, sa, 0, 127 - 8);
+            a, st.pb[i / DT], st.acc[i % DT], 4, 0, 0, sa, 0, 127);
       }
     } else {
       v8i vf = vfrag(0);
@@ -341,13 +384,14 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
         const v8i a = vf;
         if (i + 1 < 2 * DT) vf = vfrag(i + 1);
         __builtin_amdgcn_sched_barrier(0);
-        st.acc[i % DT] = mfma_fp8_scaled(a, st.pb[i / DT], st.acc[i % DT], sv_e8, 127 - 8);
+        st.acc[i % DT] = mfma_fp8_scaled(a, st.pb[i / DT], st.acc[i % DT], sv_e8, 127);
       }
     }
-    const float ell = rs[0] * (1.0f / 256.0f);
+    }
     if (VMEAN == VS_VMEAN_BLOCK) {
-      // + mu (x) l, one outer product per pair of channel tiles: lanes 0-31
-      // carry mu of tile 2pr, lanes 32-63 of tile 2pr + 1
+      // + mu (x) l_tile, one outer product per pair of channel tiles: lanes
+      // 0-31 carry mu of tile 2pr, lanes 32-63 of tile 2pr + 1, and every
+      // lane the row sum of its own query
 #pragma unroll
       for (int pr = 0; pr < DT / 2; ++pr) {
         const float mu = mub[64 * pr + c.lane];
@@ -357,7 +401,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
           c2[r] = st.acc[2 * pr][r];
           c2[16 + r] = st.acc[2 * pr + 1][r];
         }
-        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, ell, c2, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(mu, st.ell, c2, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           st.acc[2 * pr][r] = c2[r];
@@ -365,7 +409,6 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
         }
       }
     }
-    st.l = st.alpha * st.l + ell;
     // keep the products in this phase: left to itself the compiler may sink
     // them past the barrier, up to the vector phase's rescale, which then
     // reads their results a few instructions after issue (seen to give wrong
@@ -379,41 +422,72 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D>& c, State<D
 }
 
 // Vector phase V(j) of one wave, j < nb: mask (ragged last tile), tile max,
-// integer running max, O^T rescale, E4M3 probabilities of key tile j.
-template <int D, bool EXPCAST>
-__device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D>& st) {
+// the running max's update where it grew, E4M3 (or ExpCast) probabilities of
+// key tile j, the tile row sum and l.  With dbg, the lane's codes are
+// written to its row of the diagnostic code buffer.
+template <int D, bool BF, bool EXPCAST>
+__device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
+                                           uint8_t* dbg) {
   constexpr int DT = D / 32;
   if (j == c.nb - 1 && (c.S & (kBlock - 1))) mask_tile(st.s, c.S - j * kBlock, c.hh);
-  const float m_new = __builtin_fmaxf(st.m, __builtin_ceilf(tile_max(st.s)));
-  st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // a power of two (0 on tile 0)
-  if (__ballot(st.alpha != 1.0f)) {
+  const float xm = tile_max(st.s);   // max of s - m + 8 over the row's 128 keys
+  // Tile 0 sets the reference (the bias was 0, so x = s); later tiles move
+  // it where the row max grew.  tau = b - b' is the shift actually applied,
+  // so x, O^T and l stay consistent with the new bias b'.
+  const bool first = j == 0;
+  if (first || __ballot(xm > 8.0f)) {
+    const float d = (first || xm > 8.0f) ? xm - 8.0f : 0.0f;
+    const float b_new = st.b - d;
+    const float tau = st.b - b_new;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[t][r] *= st.alpha;
-  }
-  st.m = m_new;
-  if (EXPCAST) {
-    const float bias = kExpcastK0 - 8.0f * m_new;
-    // ExpCast pre-codes stay below 126.5 unless rounding of 8 m is coarse
-    // (|m| >= 2^20 log2 units): only then is the cap applied per element
-    if (__ballot(__builtin_fabsf(m_new) >= 1048576.0f)) {
+      for (int r = 0; r < 16; ++r) st.s[t][r] -= tau;
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-tau);
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        st.pb[q >> 3][q & 7] = p_codes4<true, true>(st.s[q >> 2], q & 3, bias);
-    } else {
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        st.pb[q >> 3][q & 7] = p_codes4<true, false>(st.s[q >> 2], q & 3, bias);
+        for (int r = 0; r < 16; ++r) st.acc[t][r] *= alpha;
+      st.l *= alpha;
     }
-  } else if (!__ballot(__builtin_fabsf(m_new) > 64.0f)) {
-    const float sc = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_new) - 8);
+    st.b = b_new;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) st.pb[q >> 3][q & 7] = p_codes4_fast(st.s[q >> 2], q & 3, sc);
+    for (int r = 0; r < 16; ++r) st.bias[r] = b_new;
+  }
+  float ls = 0.0f;
+  int pk[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    pk[q] = EXPCAST ? expcast_codes4(st.s[q >> 2], q & 3, ls) : p_codes4(st.s[q >> 2], q & 3, ls);
+  if constexpr (BF) {
+    // the codes' values as bf16 (exact), B operand of the bf16 PV: k-step
+    // ks takes dwords 2 ks and 2 ks + 1
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk[2 * ks], 1.0f, false);
+      const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk[2 * ks], 1.0f, true);
+      const v2bf c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk[2 * ks + 1], 1.0f, false);
+      const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk[2 * ks + 1], 1.0f, true);
+      st.pbf[ks] = v8bf{a[0], a[1], b[0], b[1], c2[0], c2[1], d[0], d[1]};
+    }
   } else {
 #pragma unroll
+    for (int q = 0; q < 16; ++q) st.pb[q >> 3][q & 7] = pk[q];
+  }
+  // the other 64 keys of the row are in lane ^ 32
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls),
+                                                    false, false);
+    ls = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  st.ell = ls;
+  st.l += ls;
+  if (dbg) {
+    // dword q holds keys 32 (q / 4) + 8 (q % 4) + 4 hh .. + 3 of the tile
+#pragma unroll
     for (int q = 0; q < 16; ++q)
-      st.pb[q >> 3][q & 7] = p_codes4<false, false>(st.s[q >> 2], q & 3, 8.0f - m_new);
+      *reinterpret_cast<int*>(dbg + j * kBlock + 32 * (q >> 2) + 8 * (q & 3) + 4 * c.hh) = pk[q];
   }
   st.ks = c.ksc[j + 1 < c.nb ? j + 1 : j];
 }
@@ -426,41 +500,43 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D>& c, State<D
 // last read in the other group's M(j - 1), which ended at the barrier before.
 //   kb: K_j (read)     kw: K_{j+1} (filled)
 //   vb: V_{j-1} (read) vw: V_j (filled)
-template <int D, bool EXPCAST, int VMEAN, bool V4>
-__device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D>& c, State<D>& st,
+template <int D, bool BF, bool EXPCAST, int VMEAN, bool V4, bool DBG>
+__device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
                                               const uint8_t* kb, uint8_t* kw,
                                               const uint8_t* vb, uint8_t* vw,
                                               const float* mub, float* muw,
-                                              const uint8_t* scb, uint8_t* scw) {
+                                              const uint8_t* scb, uint8_t* scw, uint8_t* dbg) {
   if (c.dma_wave >= 0 && j < c.nb) {
-    if (j + 1 < c.nb) issue_k<D>(c, j + 1, kw);
-    issue_v<D, VMEAN, V4>(c, j, vw, muw, scw);
+    if (j + 1 < c.nb) issue_k<D, BF>(c, j + 1, kw);
+    issue_v<D, BF, VMEAN, V4>(c, j, vw, muw, scw);
   }
-  phase_mfma<D, VMEAN, V4>(j, c, st, kb, vb, mub, scb);
+  phase_mfma<D, BF, VMEAN, V4>(j, c, st, kb, vb, mub, scb);
   __syncthreads();
-  if (j < c.nb) phase_valu<D, EXPCAST>(j, c, st);
+  if (j < c.nb) phase_valu<D, BF, EXPCAST>(j, c, st, DBG ? dbg : nullptr);
   if (c.dma_wave >= 0) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 
-template <int D, bool EXPCAST, int VMEAN, bool V4>
+template <int D, bool BF, bool EXPCAST, int VMEAN, bool V4, bool DBG>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ v_mean, const float* __restrict__ q_mu, int S, int H,
     int nb, int npairs, int total, void* __restrict__ out, int out_bf16,
-    float* __restrict__ lse2) {
-  constexpr int KD = D / 64;                 // k-steps of the QK product
+    float* __restrict__ lse2, uint8_t* __restrict__ dbg_codes, int dbg_stride) {
   constexpr int DT = D / 32;                 // 32-channel tiles of O^T
-  constexpr int TB = kBlock * D;             // bytes of one K (or V) tile
-  constexpr int KRC = D / 16;                // 16-byte chunks per K row
+  constexpr int KRB = k_row_bytes<D, BF>();
+  constexpr int KTB = kBlock * KRB;          // bytes of one K tile
+  constexpr int VTB = v_tile_bytes<D, BF, V4>();   // bytes of one V tile
+  constexpr int KRC = KRB / 16;              // 16-byte chunks per K row
+  constexpr int NKS = Ctx<D, BF>::NKS;
   // separate variables per buffer: the compiler then knows a DMA into one
   // buffer does not alias reads of the other and does not wait for it
-  __shared__ __attribute__((aligned(1024))) uint8_t sk0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sk1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[KTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[KTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[BF ? VTB : kBlock * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[BF ? VTB : kBlock * D];
   __shared__ __attribute__((aligned(16))) float smu0[D];
   __shared__ __attribute__((aligned(16))) float smu1[D];
   // MXFP4 V: the tile's E8M0 group scales, 4 bytes per channel
@@ -491,24 +567,29 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   const int qb_raw = 2 * qp + group;
   const int qb = qb_raw < nb ? qb_raw : nb - 1;
 
-  Ctx<D> c;
+  Ctx<D, BF> c;
   c.dma_wave = group == 0 ? wave : -1;
   c.lane = lane;
   c.hh = hh;
   c.nb = nb;
   c.S = S;
   const int qrow = qb * kBlock + (wave & 3) * 32 + l32;
-  {
+  if constexpr (BF) {
+    // bf16 Q: k-step ks holds channels 16 ks + 8 hh .. + 7
+    const uint16_t* qptr = reinterpret_cast<const uint16_t*>(q8) + (bh * S_pad + qrow) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      c.qb[ks] = as_v8bf(*reinterpret_cast<const uint4*>(qptr + 16 * ks));
+  } else {
     const uint8_t* qptr = q8 + (bh * S_pad + qrow) * D + 32 * hh;
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
+    for (int kd = 0; kd < NKS; ++kd)
       c.qa[kd] = make_v8i(*reinterpret_cast<const uint4*>(qptr + 64 * kd),
                           *reinterpret_cast<const uint4*>(qptr + 64 * kd + 16));
+    c.q_e8 = e8m0_of(q_scale[bh * nb + qb]);
   }
-  c.q_e8 = e8m0_of(q_scale[bh * nb + qb]);
-  c.krs = make_rsrc(k8 + bh * S_pad * D, S_pad * D);
-  c.vrs = V4 ? make_rsrc(v8 + bh * S_pad * D / 2, S_pad * D / 2)
-             : make_rsrc(v8 + bh * S_pad * D, S_pad * D);
+  c.krs = make_rsrc(k8 + bh * S_pad * KRB, S_pad * KRB);
+  c.vrs = make_rsrc(v8 + bh * nb * VTB, static_cast<size_t>(nb) * VTB);
   c.scrs = make_rsrc(V4 ? reinterpret_cast<const uint8_t*>(v_scale) + bh * nb * D * 4
                         : reinterpret_cast<const uint8_t*>(v_scale),
                      V4 ? nb * D * 4 : 0);
@@ -516,33 +597,52 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
                      VMEAN == VS_VMEAN_BLOCK ? nb * D * sizeof(float) : 0);
   c.ksc = k_scale + bh * nb;
   c.vsc = v_scale + bh * nb;
-  c.k_src[0] = dma_src_chunk<KRC>(lane, 0) * 16;
-  c.k_src[1] = dma_src_chunk<KRC>(lane, 1) * 16;
-  c.v_src[0] = dma_src_chunk<V4 ? 4 : 8>(lane, 0) * 16;
-  c.v_src[1] = dma_src_chunk<V4 ? 4 : 8>(lane, 1) * 16;
+#pragma unroll
+  for (int i = 0; i < (KRC == 16 ? 4 : 2); ++i) c.k_src[i] = dma_src_chunk<KRC>(lane, i) * 16;
+#pragma unroll
+  for (int i = 0; i < (BF ? 4 : 2); ++i)
+    c.v_src[i] = dma_src_chunk<BF ? 16 : V4 ? 4 : 8>(lane, i) * 16;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
     c.v4_rd[kk] = l32 * 64 + (((2 * kk + hh) ^ row_swz<4>(l32)) << 4);
+  if constexpr (BF) {
+    // A operand of k-step ks: key l32, channels 16 ks + 8 hh .. + 7 (chunk 2 ks + hh)
 #pragma unroll
-  for (int kd = 0; kd < KD; ++kd)
+    for (int ks = 0; ks < NKS; ++ks)
+      c.k_rd[ks][0] = l32 * KRB + (((2 * ks + hh) ^ row_swz<KRC>(l32)) << 4);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      c.k_rd[kd][e] = l32 * D + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
+    for (int kd = 0; kd < NKS; ++kd)
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+      for (int e = 0; e < 2; ++e)
+        c.k_rd[kd][BF ? 0 : e] = l32 * KRB + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
+  }
+  if constexpr (BF) {
+    // bf16 V rows of 256 bytes: k-step ks of lane half hh is chunk 2 ks + hh
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      c.v_rd[kk][e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
+    for (int ks = 0; ks < 8; ++ks)
+      c.v_rd[ks][0] = l32 * 256 + (((2 * ks + hh) ^ row_swz<16>(l32)) << 4);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    c.ones[i] = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        c.v_rd[kk][BF ? 0 : e] = l32 * kBlock + (((4 * kk + 2 * hh + e) ^ row_swz<8>(l32)) << 4);
+  }
 
-  State<D> st;
+  // diagnostic codes of this lane's row (every dbg_stride-th valid row)
+  uint8_t* dbg = nullptr;
+  if (DBG && qb_raw < nb && qrow < S && qrow % dbg_stride == 0)
+    dbg = dbg_codes + (bh * ((S + dbg_stride - 1) / dbg_stride) + qrow / dbg_stride) * S_pad;
+
+  State<D, BF> st;
   st.ks = c.ksc[0];
   st.vs = V4 ? 1.0f : c.vsc[0];
-  st.m = -INFINITY;
+  st.b = 0.0f;
   st.l = 0.0f;
-  st.alpha = 1.0f;
+  st.ell = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st.bias[r] = 0.0f;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -550,7 +650,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 
   // ---- prologue: K of tile 0; group 1 runs one phase behind group 0 ----
   if (c.dma_wave >= 0) {
-    issue_k<D>(c, 0, sk0);
+    issue_k<D, BF>(c, 0, sk0);
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
@@ -558,10 +658,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 
   // ---- nb + 1 trips, two per loop iteration (static buffer roles) ----
   for (int j = 0; j <= nb; j += 2) {
-    pingpong_trip<D, EXPCAST, VMEAN, V4>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0, ssc1, ssc0);
+    pingpong_trip<D, BF, EXPCAST, VMEAN, V4, DBG>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0,
+                                                    ssc1, ssc0, dbg);
     if (j + 1 <= nb)
-      pingpong_trip<D, EXPCAST, VMEAN, V4>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0, smu1, ssc0,
-                                           ssc1);
+      pingpong_trip<D, BF, EXPCAST, VMEAN, V4, DBG>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0,
+                                                      smu1, ssc0, ssc1, dbg);
   }
   if (group == 0) __syncthreads();
 
@@ -595,27 +696,105 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
           *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + d0) = o;
         }
       }
+    // m = 8 - b and l in units of 2^8 p: lse2 = m + log2(l) - 8 + q_mu
     if (hh == 0)
-      lse2[bh * S + qrow] =
-          st.m + __builtin_amdgcn_logf(st.l) + (q_mu ? q_mu[bh * S + qrow] : 0.0f);
+      lse2[bh * S + qrow] = __builtin_amdgcn_logf(st.l) - st.b + (q_mu ? q_mu[bh * S + qrow] : 0.0f);
   }
 }
 
-template <int D, bool EXPCAST, bool V4>
-void launch_vm(int vmean_mode, int total, hipStream_t st, const uint8_t* q8, const float* qs,
-               const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
-               const float* vm, const float* qmu, int S, int H, int nb, int npairs,
-               void* out, int out_bf16, float* lse2) {
-  const dim3 grid(total), block(512);
-  if (vmean_mode == VS_VMEAN_BLOCK)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_BLOCK, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
-  else if (vmean_mode == VS_VMEAN_SEQ)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_SEQ, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, EXPCAST, VS_VMEAN_NONE, V4>), grid, block, 0, st, q8,
-                       qs, k8, ks, v8, vs, vm, qmu, S, H, nb, npairs, total, out, out_bf16, lse2);
+struct Launch {
+  int total, S, H, nb, npairs, out_bf16, dbg_stride;
+  hipStream_t st;
+  const uint8_t *q8, *k8, *v8;
+  const float *qs, *ks, *vs, *vm, *qmu;
+  void* out;
+  float* lse2;
+  uint8_t* dbg;
+};
+
+template <int D, bool BF, bool EXPCAST, bool V4, bool DBG>
+void launch_vm(int vmean_mode, const Launch& a) {
+  const dim3 grid(a.total), block(512);
+#define VS_LAUNCH(VM)                                                                             \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF, EXPCAST, VM, V4, DBG>), grid, block, 0, a.st,     \
+                     a.q8, a.qs, a.k8, a.ks, a.v8, a.vs, a.vm, a.qmu, a.S, a.H, a.nb, a.npairs,    \
+                     a.total, a.out, a.out_bf16, a.lse2, a.dbg, a.dbg_stride)
+  if (vmean_mode == VS_VMEAN_BLOCK) VS_LAUNCH(VS_VMEAN_BLOCK);
+  else if (vmean_mode == VS_VMEAN_SEQ) VS_LAUNCH(VS_VMEAN_SEQ);
+  else VS_LAUNCH(VS_VMEAN_NONE);
+#undef VS_LAUNCH
+}
+
+int attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+             const uint8_t* v8, const float* v_scale, const float* v_mean, int vmean_mode,
+             const float* q_mu, int B, int S, int H, int D, unsigned flags, void* out,
+             float* lse2, uint8_t* dbg, int dbg_stride, void* stream) {
+  if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
+  if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
+    return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_EXPCAST | VS_V_MXFP4 | VS_OUT_BF16 | VS_BF16_MMA)) return VS_ERR_INVALID_ARG;
+  if (dbg && dbg_stride < 1) return VS_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
+  if (dbg && (flags & VS_V_MXFP4)) return VS_ERR_UNSUPPORTED;
+  // the bf16 products take V as bf16 values, whatever format quantized it
+  if ((flags & VS_BF16_MMA) && (flags & VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
+  if (B == 0 || S == 0 || H == 0) return VS_OK;
+  if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
+  const bool qk16 = (flags & VS_BF16_MMA) != 0;
+  if (!q8 || (!qk16 && !q_scale) || !k8 || (!qk16 && !k_scale) || !v8 || !v_scale || !out || !lse2)
+    return VS_ERR_INVALID_ARG;
+  const void* ptrs[] = {q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, out, lse2, dbg};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
+  const int nb = n_blocks(S);
+  // one workgroup per (batch, head, pair of 128-query blocks)
+  const int npairs = (nb + 1) / 2;
+  const long long total = static_cast<long long>(B) * H * npairs;
+  if (total > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
+  // one head's K and V (codes or bf16) are addressed through 32-bit buffer ranges
+  if (static_cast<long long>(nb) * kBlock * D * (qk16 ? 2 : 1) > 0x7FFFFFFFLL)
+    return VS_ERR_UNSUPPORTED;
+
+  Launch a;
+  a.total = static_cast<int>(total);
+  a.S = S; a.H = H; a.nb = nb; a.npairs = npairs;
+  a.out_bf16 = (flags & VS_OUT_BF16) != 0;
+  a.dbg_stride = dbg ? dbg_stride : 1;
+  a.st = as_stream(stream);
+  a.q8 = q8; a.k8 = k8; a.v8 = v8;
+  // the bf16 form carries the Q and K scales in its values; the kernel
+  // never reads them then (the block scale loads are kept in range)
+  a.qs = q_scale ? q_scale : v_scale;
+  a.ks = k_scale ? k_scale : v_scale;
+  a.vs = v_scale; a.vm = v_mean; a.qmu = q_mu;
+  a.out = out; a.lse2 = lse2; a.dbg = dbg;
+  const bool ec = (flags & VS_EXPCAST) != 0, v4 = (flags & VS_V_MXFP4) != 0;
+  const int sel = (D == 128 ? 8 : 0) | (qk16 ? 4 : 0) | (ec ? 2 : 0) | (v4 ? 1 : 0);
+  if (dbg) {
+    switch (sel) {
+      case 0: launch_vm<64, false, false, false, true>(vmean_mode, a); break;
+      case 2: launch_vm<64, false, true, false, true>(vmean_mode, a); break;
+      case 4: launch_vm<64, true, false, false, true>(vmean_mode, a); break;
+      case 6: launch_vm<64, true, true, false, true>(vmean_mode, a); break;
+      case 8: launch_vm<128, false, false, false, true>(vmean_mode, a); break;
+      case 10: launch_vm<128, false, true, false, true>(vmean_mode, a); break;
+      case 12: launch_vm<128, true, false, false, true>(vmean_mode, a); break;
+      default: launch_vm<128, true, true, false, true>(vmean_mode, a); break;
+    }
+    return launch_status();
+  }
+  switch (sel) {
+#define VS_A(n, d, q, e, v) case n: launch_vm<d, q, e, v, false>(vmean_mode, a); break;
+    VS_A(0, 64, false, false, false) VS_A(1, 64, false, false, true)
+    VS_A(2, 64, false, true, false) VS_A(3, 64, false, true, true)
+    VS_A(4, 64, true, false, false) VS_A(6, 64, true, true, false)
+    VS_A(8, 128, false, false, false) VS_A(9, 128, false, false, true)
+    VS_A(10, 128, false, true, false) VS_A(11, 128, false, true, true)
+    VS_A(12, 128, true, false, false)
+    default: launch_vm<128, true, true, false, false>(vmean_mode, a); break;
+#undef VS_A
+  }
+  return launch_status();
 }
 
 }  // namespace
@@ -626,43 +805,18 @@ extern "C" int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const ui
                                const float* v_mean, int vmean_mode, const float* q_mu, int B,
                                int S, int H, int D, unsigned flags, void* out, float* lse2,
                                void* stream) {
-  using namespace vs;
-  if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
-  if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
-    return VS_ERR_INVALID_ARG;
-  if (flags & ~(VS_EXPCAST | VS_V_MXFP4 | VS_OUT_BF16)) return VS_ERR_INVALID_ARG;
-  if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
-  if (B == 0 || S == 0 || H == 0) return VS_OK;
-  if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
-  if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !out || !lse2)
-    return VS_ERR_INVALID_ARG;
-  const void* ptrs[] = {q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, out, lse2};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
-  const int nb = n_blocks(S);
-  // one workgroup per (batch, head, pair of 128-query blocks)
-  const int npairs = (nb + 1) / 2;
-  const long long total = static_cast<long long>(B) * H * npairs;
-  if (total > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
-  // one head's codes are addressed through a 32-bit buffer range
-  if (static_cast<long long>(nb) * kBlock * D > 0x7FFFFFFFLL) return VS_ERR_UNSUPPORTED;
+  return vs::attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, B, S, H, D,
+                      flags, out, lse2, nullptr, 0, stream);
+}
 
-  hipStream_t st = as_stream(stream);
-  const bool ec = (flags & VS_EXPCAST) != 0, v4 = (flags & VS_V_MXFP4) != 0;
-  const int tot = static_cast<int>(total);
-  const int out_bf16 = (flags & VS_OUT_BF16) != 0;
-#define VS_ATTN_ARGS vmean_mode, tot, st, q8, q_scale, k8, k_scale, v8, v_scale, v_mean, q_mu, S, \
-    H, nb, npairs, out, out_bf16, lse2
-  switch ((D == 128 ? 4 : 0) | (ec ? 2 : 0) | (v4 ? 1 : 0)) {
-    case 0: launch_vm<64, false, false>(VS_ATTN_ARGS); break;
-    case 1: launch_vm<64, false, true>(VS_ATTN_ARGS); break;
-    case 2: launch_vm<64, true, false>(VS_ATTN_ARGS); break;
-    case 3: launch_vm<64, true, true>(VS_ATTN_ARGS); break;
-    case 4: launch_vm<128, false, false>(VS_ATTN_ARGS); break;
-    case 5: launch_vm<128, false, true>(VS_ATTN_ARGS); break;
-    case 6: launch_vm<128, true, false>(VS_ATTN_ARGS); break;
-    default: launch_vm<128, true, true>(VS_ATTN_ARGS); break;
-  }
-#undef VS_ATTN_ARGS
-  return launch_status();
+extern "C" int vs_fp8_attn_fwd_pcodes(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                      const float* k_scale, const uint8_t* v8,
+                                      const float* v_scale, const float* v_mean, int vmean_mode,
+                                      const float* q_mu, int B, int S, int H, int D,
+                                      unsigned flags, void* out, float* lse2, uint8_t* p_codes,
+                                      int row_stride, void* stream) {
+  if (!p_codes && B > 0 && S > 0 && H > 0) return VS_ERR_INVALID_ARG;
+  if (row_stride < 1) return VS_ERR_INVALID_ARG;
+  return vs::attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, v_mean, vmean_mode, q_mu, B, S, H, D,
+                      flags, out, lse2, p_codes, row_stride, stream);
 }

@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old) 
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HI));
 }
 
+// Two float32 values -> two bf16 (round to nearest even) packed low, high.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const v2bf16 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  uint32_t r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+
 __device__ __forceinline__ float clamp448(float x) {
   return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
 }

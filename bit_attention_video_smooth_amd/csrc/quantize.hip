@@ -182,8 +182,12 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
 // token rows.  With q_mu != nullptr also q_mu[s] = c * (q_s . k_mean) from
 // the bf16 q.  PERM: rows gathered through perm (K only).  HAD: rows
 // rotated by H_D after the centring and before the scaling by pre (the
-// caller folds Q's 1/D into pre).
-template <int D, bool PERM, bool HAD>
+// caller folds Q's 1/D into pre).  B16: instead of the E4M3 bytes, each
+// code's value times the block scale as bf16 (2 bytes per element, same
+// row layout): E4M3 values carry 4 significant bits, so the bf16 is exact
+// whenever the smallest code times the scale is a bf16 number
+// (scale >= 2^-124).
+template <int D, bool PERM, bool HAD, bool B16>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
@@ -234,6 +238,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   if (threadIdx.x == 0) scale_out[bh * nb + j] = ldexpf(1.0f, ex);
 
   const size_t S_pad = static_cast<size_t>(nb) * kBlock;
+  const float sc = ldexpf(1.0f, ex);
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int tok = j * kBlock + r + ROWS * i;
@@ -242,7 +247,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     w0 = cvt_pk_e4m3<true>(clamp448(val[i][2] * inv), clamp448(val[i][3] * inv), w0);
     w1 = cvt_pk_e4m3<false>(clamp448(val[i][4] * inv), clamp448(val[i][5] * inv), w1);
     w1 = cvt_pk_e4m3<true>(clamp448(val[i][6] * inv), clamp448(val[i][7] * inv), w1);
-    *reinterpret_cast<uint2*>(codes + (bh * S_pad + tok) * D + 8 * c) = make_uint2(w0, w1);
+    if (B16) {
+      // decoded values (hardware E4M3 -> f32, exact), times the power-of-two
+      // scale (exact), rounded to bf16 (nearest even; exact here)
+      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
+      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
+      const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
+      const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);
+      const uint32_t o[4] = {f32x2_to_bf16x2(f0[0] * sc, f0[1] * sc),
+                             f32x2_to_bf16x2(f1[0] * sc, f1[1] * sc),
+                             f32x2_to_bf16x2(f2[0] * sc, f2[1] * sc),
+                             f32x2_to_bf16x2(f3[0] * sc, f3[1] * sc)};
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(codes) + (bh * S_pad + tok) * D + 8 * c) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      *reinterpret_cast<uint2*>(codes + (bh * S_pad + tok) * D + 8 * c) = make_uint2(w0, w1);
+    }
   }
 }
 
@@ -259,6 +279,38 @@ __device__ __forceinline__ uint32_t fp4_code(float x) {
   const uint32_t hi = min(r - 252u, 7u);
   const uint32_t lo = static_cast<uint32_t>(__builtin_rintf(2.0f * m));
   return (m < 1.0f ? lo : hi) | (__float_as_uint(x) >> 31 << 3);
+}
+
+// Value of an E2M1 nibble (sign in bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float fp4_value(uint32_t code) {
+  const uint32_t m = code & 7u;
+  const float mag = m < 2u ? 0.5f * static_cast<float>(m)
+                           : ldexpf(1.0f + 0.5f * static_cast<float>(m & 1u), static_cast<int>(m >> 1) - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+// The bf16 V tile in LDS: channel row d of 128 tokens, 8-byte units (4
+// tokens) XOR-swizzled by d / 8 so that the 16 channel groups of a wave's
+// stores fall on different banks.  Token tau sits at position p16(tau):
+// bits 2 and 3 of tau swapped (the bf16 PV product's k order); the four
+// tokens 4a .. 4a + 3 of a quad stay together in unit
+// 4 (a / 4) + ((a / 2) % 2) + 2 (a % 2).
+__device__ __forceinline__ int quad_unit16(int a) { return 4 * (a >> 2) + ((a >> 1) & 1) + 2 * (a & 1); }
+
+__device__ __forceinline__ void store_quad16(uint16_t* tile16, int d, int a, const float (&x)[4]) {
+  const int u = quad_unit16(a) ^ ((d >> 3) & 31);
+  *reinterpret_cast<uint2*>(tile16 + d * kBlock + 4 * u) =
+      make_uint2(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]));
+}
+
+// The LDS tile, unswizzled, to its global [D][128] bf16 place.
+template <int D>
+__device__ __forceinline__ void copy_out16(const uint16_t* tile16, uint16_t* dst) {
+  for (int g = threadIdx.x; g < D * kBlock / 4; g += 256) {
+    const int d = g >> 5, u = g & 31;
+    *reinterpret_cast<uint2*>(dst + 4 * g) =
+        *reinterpret_cast<const uint2*>(tile16 + d * kBlock + 4 * (u ^ ((d >> 3) & 31)));
+  }
 }
 
 // Smallest e >= -127 with amax <= 6 * 2^e (0 when amax == 0).
@@ -305,7 +357,13 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
 // the k order of the 4-bit A operand of the FP8/FP4 matrix core -- nibble
 // q (low nibble first) is token 8 ((q % 16) / 4) + 4 (q / 16) + q % 4 of
 // the group -- and scale_out is u8 [B,H,nb,D,4], byte g = e + 127.
-template <int D, bool OWN_MEAN, bool PERM, bool FP4>
+//
+// B16 (VS_BF16_MMA): instead of the codes, each quantized residual's value
+// (the E4M3 or E2M1 code's value times its scale, exact in bf16) as bf16,
+// per block a D x 128 tile with token tau of a channel row at position
+// p16(tau) (bits 2 and 3 of tau swapped: the k order of the bf16 matrix
+// core's PV product); scale_out as without it.
+template <int D, bool OWN_MEAN, bool PERM, bool FP4, bool B16>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
@@ -314,7 +372,8 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
   constexpr int QR = 256 / CH;           // quads in flight per pass
   constexpr int NQ = kBlock / 4 / QR;    // quads per thread
   __shared__ float red4[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[D * kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[B16 ? 16 : D * kBlock];
+  __shared__ __attribute__((aligned(16))) uint16_t tile16[B16 ? D * kBlock : 8];
   __shared__ double part[OWN_MEAN ? QR : 1][OWN_MEAN ? D : 1];
   __shared__ float smean[OWN_MEAN ? D : 1];
   const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
@@ -417,24 +476,42 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
           static_cast<uint8_t>(ex + 127);
     }
     __syncthreads();
+    if constexpr (B16) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const int a = a0 + QR * n, g = a >> 3;
-      // the quad's four nibbles: bytes 8 (a % 2) + 2 ((a % 8) / 2) of the group
-      const int off = 16 * g + 8 * (a & 1) + 2 * ((a & 7) >> 1);
+      for (int n = 0; n < NQ; ++n) {
+        const int a = a0 + QR * n, g = a >> 3;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float inv = ldexpf(1.0f, -gexp[g][8 * c + e]);
-        uint32_t w = 0;
+        for (int e = 0; e < 8; ++e) {
+          const int ex = gexp[g][8 * c + e];
+          const float inv = ldexpf(1.0f, -ex), sc = ldexpf(1.0f, ex);
+          float x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w |= fp4_code(val[n][q][e] * inv) << (4 * q);
-        *reinterpret_cast<uint16_t*>(tile4 + (8 * c + e) * 64 + off) = static_cast<uint16_t>(w);
+          for (int q = 0; q < 4; ++q) x[q] = fp4_value(fp4_code(val[n][q][e] * inv)) * sc;
+          store_quad16(tile16, 8 * c + e, a, x);
+        }
       }
+      __syncthreads();
+      copy_out16<D>(tile16, reinterpret_cast<uint16_t*>(codes) + (bh * nb + j) * static_cast<size_t>(D) * kBlock);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const int a = a0 + QR * n, g = a >> 3;
+        // the quad's four nibbles: bytes 8 (a % 2) + 2 ((a % 8) / 2) of the group
+        const int off = 16 * g + 8 * (a & 1) + 2 * ((a & 7) >> 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float inv = ldexpf(1.0f, -gexp[g][8 * c + e]);
+          uint32_t w = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w |= fp4_code(val[n][q][e] * inv) << (4 * q);
+          *reinterpret_cast<uint16_t*>(tile4 + (8 * c + e) * 64 + off) = static_cast<uint16_t>(w);
+        }
+      }
+      __syncthreads();
+      uint4* dst = reinterpret_cast<uint4*>(codes + (bh * nb + j) * static_cast<size_t>(D) * 64);
+      for (int idx = threadIdx.x; idx < D * 64 / 16; idx += 256)
+        dst[idx] = *reinterpret_cast<const uint4*>(tile4 + 16 * idx);
     }
-    __syncthreads();
-    uint4* dst = reinterpret_cast<uint4*>(codes + (bh * nb + j) * static_cast<size_t>(D) * 64);
-    for (int idx = threadIdx.x; idx < D * 64 / 16; idx += 256)
-      dst[idx] = *reinterpret_cast<const uint4*>(tile4 + 16 * idx);
     return;
   }
   float a = 0.0f;
@@ -449,6 +526,32 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
   const float inv = ldexpf(1.0f, -e);
   if (threadIdx.x == 0) scale_out[bh * nb + j] = ldexpf(1.0f, e);
 
+  if constexpr (B16) {
+    const float sc = ldexpf(1.0f, e);
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      float x[8][4];                       // channel e2, token q of the quad
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* v = val[n][q];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t w = cvt_pk_e4m3<false>(clamp448(v[4 * h2] * inv), clamp448(v[4 * h2 + 1] * inv), 0u);
+          w = cvt_pk_e4m3<true>(clamp448(v[4 * h2 + 2] * inv), clamp448(v[4 * h2 + 3] * inv), w);
+          const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+          const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+          x[4 * h2 + 0][q] = f0[0] * sc;
+          x[4 * h2 + 1][q] = f0[1] * sc;
+          x[4 * h2 + 2][q] = f1[0] * sc;
+          x[4 * h2 + 3][q] = f1[1] * sc;
+        }
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) store_quad16(tile16, 8 * c + e2, a0 + QR * n, x[e2]);
+    }
+    __syncthreads();
+    copy_out16<D>(tile16, reinterpret_cast<uint16_t*>(codes) + (bh * nb + j) * static_cast<size_t>(D) * kBlock);
+  } else {
 #pragma unroll
   for (int n = 0; n < NQ; ++n) {
     uint32_t lo[4], hi[4];                 // token q: channels 0-3, 4-7
@@ -477,6 +580,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
     const int row = idx >> 3, ch = idx & 7;
     dst[idx] = *reinterpret_cast<const uint4*>(tile + row * kBlock + ((ch ^ ((row >> 3) & 7)) << 4));
   }
+  }
 }
 
 }  // namespace
@@ -485,7 +589,7 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
 namespace vs {
 namespace {
 
-template <int D, bool PERM, bool HAD, bool FP4>
+template <int D, bool PERM, bool HAD, bool FP4, bool B16>
 void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, const uint16_t* q,
                   const uint16_t* k, const uint16_t* v, int kv_layout, int S, int H, int nb,
                   float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
@@ -494,16 +598,16 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
   const dim3 block(256);
   // with the rotation Q carries its 1/D (a power of two: exact)
   const float q_pre = HAD ? c_log2 * (1.0f / D) : c_log2;
-  hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD>), gq.grid, block, 0, st, q,
+  hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD, B16>), gq.grid, block, 0, st, q,
                      VS_LAYOUT_BSHD, S, H, nb, nullptr, q_pre, q8, q_scale, k_mean,
                      k_mean ? q_mu : nullptr, c_log2, gq.hfast, nullptr);
-  hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD>), gkv.grid, block, 0, st, k, kv_layout, S,
+  hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD, B16>), gkv.grid, block, 0, st, k, kv_layout, S,
                      H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
   if (vmean_mode == VS_VMEAN_BLOCK_OUT)
-    hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM, FP4>), gkv.grid, block, 0, st, v, kv_layout,
-                       S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+    hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM, FP4, B16>), gkv.grid, block, 0, st, v,
+                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
   else
-    hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM, FP4>), gkv.grid, block, 0, st, v,
+    hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM, FP4, B16>), gkv.grid, block, 0, st, v,
                        kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
 }
 
@@ -516,7 +620,7 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (perm && kv_layout != VS_LAYOUT_BSHD) return VS_ERR_INVALID_ARG;
-  if (flags & ~(VS_QK_HADAMARD | VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_QK_HADAMARD | VS_V_MXFP4 | VS_BF16_MMA)) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
       vmean_mode != VS_VMEAN_BLOCK_OUT)
     return VS_ERR_INVALID_ARG;
@@ -539,25 +643,29 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
 #define VS_QUANT_ARGS gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean, \
     vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm
   const bool had = (flags & VS_QK_HADAMARD) != 0, fp4 = (flags & VS_V_MXFP4) != 0;
-  // (D, permutation, rotation, FP4 V) -> one instantiation
-  const int sel = (D == 128 ? 8 : 0) | (perm ? 4 : 0) | (had ? 2 : 0) | (fp4 ? 1 : 0);
+  const bool b16 = (flags & VS_BF16_MMA) != 0;
+  // (D, permutation, rotation, FP4 V, bf16 Q/K) -> one instantiation
+  const int sel = (D == 128 ? 16 : 0) | (b16 ? 8 : 0) | (perm ? 4 : 0) | (had ? 2 : 0) | (fp4 ? 1 : 0);
   switch (sel) {
-    case 0: launch_quant<64, false, false, false>(VS_QUANT_ARGS); break;
-    case 1: launch_quant<64, false, false, true>(VS_QUANT_ARGS); break;
-    case 2: launch_quant<64, false, true, false>(VS_QUANT_ARGS); break;
-    case 3: launch_quant<64, false, true, true>(VS_QUANT_ARGS); break;
-    case 4: launch_quant<64, true, false, false>(VS_QUANT_ARGS); break;
-    case 5: launch_quant<64, true, false, true>(VS_QUANT_ARGS); break;
-    case 6: launch_quant<64, true, true, false>(VS_QUANT_ARGS); break;
-    case 7: launch_quant<64, true, true, true>(VS_QUANT_ARGS); break;
-    case 8: launch_quant<128, false, false, false>(VS_QUANT_ARGS); break;
-    case 9: launch_quant<128, false, false, true>(VS_QUANT_ARGS); break;
-    case 10: launch_quant<128, false, true, false>(VS_QUANT_ARGS); break;
-    case 11: launch_quant<128, false, true, true>(VS_QUANT_ARGS); break;
-    case 12: launch_quant<128, true, false, false>(VS_QUANT_ARGS); break;
-    case 13: launch_quant<128, true, false, true>(VS_QUANT_ARGS); break;
-    case 14: launch_quant<128, true, true, false>(VS_QUANT_ARGS); break;
-    default: launch_quant<128, true, true, true>(VS_QUANT_ARGS); break;
+#define VS_Q(n, d, b, p, h, f) case n: launch_quant<d, p, h, f, b>(VS_QUANT_ARGS); break;
+    VS_Q(0, 64, false, false, false, false) VS_Q(1, 64, false, false, false, true)
+    VS_Q(2, 64, false, false, true, false) VS_Q(3, 64, false, false, true, true)
+    VS_Q(4, 64, false, true, false, false) VS_Q(5, 64, false, true, false, true)
+    VS_Q(6, 64, false, true, true, false) VS_Q(7, 64, false, true, true, true)
+    VS_Q(8, 64, true, false, false, false) VS_Q(9, 64, true, false, false, true)
+    VS_Q(10, 64, true, false, true, false) VS_Q(11, 64, true, false, true, true)
+    VS_Q(12, 64, true, true, false, false) VS_Q(13, 64, true, true, false, true)
+    VS_Q(14, 64, true, true, true, false) VS_Q(15, 64, true, true, true, true)
+    VS_Q(16, 128, false, false, false, false) VS_Q(17, 128, false, false, false, true)
+    VS_Q(18, 128, false, false, true, false) VS_Q(19, 128, false, false, true, true)
+    VS_Q(20, 128, false, true, false, false) VS_Q(21, 128, false, true, false, true)
+    VS_Q(22, 128, false, true, true, false) VS_Q(23, 128, false, true, true, true)
+    VS_Q(24, 128, true, false, false, false) VS_Q(25, 128, true, false, false, true)
+    VS_Q(26, 128, true, false, true, false) VS_Q(27, 128, true, false, true, true)
+    VS_Q(28, 128, true, true, false, false) VS_Q(29, 128, true, true, false, true)
+    VS_Q(30, 128, true, true, true, false)
+    default: launch_quant<128, true, true, true, true>(VS_QUANT_ARGS); break;
+#undef VS_Q
   }
 #undef VS_QUANT_ARGS
   return launch_status();

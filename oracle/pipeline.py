@@ -38,7 +38,7 @@ def default_scale(D: int) -> np.float32:
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
                             qk_hadamard=False, v_format="e4m3", expcast=False, pcast=None,
-                            fp32=True):
+                            fp32=True, trace=False):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
@@ -49,6 +49,9 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     v_format: "e4m3" (per-block power-of-two scale) or "mxfp4" (E2M1 codes
     with an E8M0 scale per 32 tokens and channel, ``fp4``).  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
+    trace: also return the E4M3 probability codes of the evaluated rows
+    ("p_codes", [R, S], key order of the (permuted) K) and the running max
+    per tile.
     Returns a dict with O, lse2 and every intermediate the GPU path also
     produces.
     """
@@ -120,12 +123,15 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
 
     if pcast is None:
         pcast = "expcast" if expcast else "e4m3"
-    o, lse2 = attention.tiled_attention(
+    res = attention.tiled_attention(
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
         e4m3.decode(k_codes), k_scale, v_hat, v_hat_scale, S, 1.0,
         v_mean=v_mean, vmean_mode=vmean_mode, q_off=q_off, pcast=pcast,
-        fp32=fp32)
-    out["O"], out["lse2"] = o, lse2
+        fp32=fp32, return_trace=trace)
+    out["O"], out["lse2"] = res[0], res[1]
+    if trace and pcast != "none":
+        out["p_codes"] = attention.p_codes_row_major(res[2], S)
+        out["tile_max"] = np.stack(res[2]["m"], axis=1)
     return out
 
 

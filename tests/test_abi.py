@@ -69,12 +69,27 @@ def test_attn_argument_errors(lib):
     assert f(*args(B=-1)) == 1
     assert f(*args(mode=1)) == 1                      # block mean without a buffer
     assert f(*args(mode=7, vm=fake)) == 1
-    assert f(*args(flags=8)) == 1
+    assert f(*args(flags=16)) == 1
     assert f(*args(flags=4, D=96)) == 2                # bf16 output: a valid flag
+    assert f(*args(flags=8, D=96)) == 2                # bf16 QK operands: a valid flag
     assert f(*args(flags=3, D=96)) == 2                # ExpCast with MXFP4 V: a valid flag pair
     assert f(*args(q8=ctypes.c_void_p(0x1004))) == 2  # misaligned
     assert f(*args(S=0)) == 0                         # empty problem
     assert f(*args(S=0, D=96)) == 2
+
+
+def test_pcodes_argument_errors(lib):
+    """The diagnostic entry point: a code buffer and a positive stride are
+    required, MXFP4 V is not supported; all rejected on the host."""
+    f = lib.vs_fp8_attn_fwd_pcodes
+    fake = ctypes.c_void_p(0x1000)
+    args = lambda **kw: [fake, fake, fake, fake, fake, fake, None, 0, None, 1, 256, 1,  # noqa: E731
+                         kw.get("D", 128), kw.get("flags", 0), fake, fake,
+                         kw.get("codes", fake), kw.get("stride", 1), None]
+    assert f(*args(codes=None)) == 1
+    assert f(*args(stride=0)) == 1
+    assert f(*args(flags=2)) == 2
+    assert f(*args(D=96)) == 2
 
 
 def test_quant_stats_kmeans_argument_errors(lib):
@@ -113,6 +128,8 @@ def test_quant_stats_kmeans_argument_errors(lib):
                        fake, fake, fake, fake, fake, fake, None, None]
     assert qe(*ex(layout=1, perm=fake)) == 1            # a permutation needs BSHD input
     assert qe(*ex(flags=4)) == 1                        # no such flag
+    assert qe(*ex(flags=16)) == 1
+    assert qe(*ex(flags=8, D=96)) == 2                  # bf16 Q/K: a valid flag
     assert qe(*ex(flags=1, D=96)) == 2
     k = lib.vs_kmeans_permute
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, None, fake, 1 << 30, None) == 1
@@ -126,7 +143,7 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
                  "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD",
-                 "VS_V_MXFP4", "VS_OUT_BF16"]:
+                 "VS_V_MXFP4", "VS_OUT_BF16", "VS_BF16_MMA"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
 

@@ -2,7 +2,8 @@
 the unsmoothed FP8 path, at the five workloads' full sizes (TeleFuser PR
 #40, "Smooth Attention Kernel Accuracy": smoothing lowers the attention
 output error).  Reported per workload and head: relative L2, MSE, cosine
-and SQNR of O with smoothing on and off; for the ExpCast workload also the
+and SQNR of O with smoothing on and off; smoothed with QK^T on the bf16
+matrix core; for the ExpCast workload also the
 smoothed path with ExpCast off; the smoothed path with the QK Hadamard
 rotation; smoothed and unsmoothed with the V residual in MXFP4; for the video-grid workloads also the
 smoothed path grouped by the static 2x8x8 spatiotemporal cube instead; the
@@ -27,13 +28,14 @@ OFFSET_K = {"tiny", "mid"}
 CUBE = (2, 8, 8)
 
 
-def _outputs(w, q, k, v, smooth, expcast=None, cube=None, qk_hadamard=False, v_format="e4m3"):
+def _outputs(w, q, k, v, smooth, expcast=None, cube=None, qk_hadamard=False, v_format="e4m3",
+             mma="fp8"):
     import bit_attention_video_smooth_amd as vs
     d = dev()
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, smooth=smooth,
                    kmeans=w.kmeans if smooth and cube is None else None,
                    expcast=w.expcast if expcast is None else expcast, cube=cube,
-                   qk_hadamard=qk_hadamard, v_format=v_format)
+                   qk_hadamard=qk_hadamard, v_format=v_format, mma=mma)
     plan.run(q, k, v)
     torch.cuda.synchronize(d)
     return plan.out
@@ -46,7 +48,8 @@ def test_smoothed_vs_unsmoothed_against_dense(name):
     print(f"[accuracy] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={w.expcast}",
           flush=True)
     q, k, v = workloads.generate(w, device=d)
-    cases = {"smoothed": _outputs(w, q, k, v, True), "unsmoothed": _outputs(w, q, k, v, False)}
+    cases = {"smoothed": _outputs(w, q, k, v, True), "unsmoothed": _outputs(w, q, k, v, False),
+             "smoothed, bf16 QK": _outputs(w, q, k, v, True, mma="bf16")}
     if w.expcast:
         cases["smoothed, ExpCast off"] = _outputs(w, q, k, v, True, expcast=False)
     cases["smoothed, QK Hadamard"] = _outputs(w, q, k, v, True, qk_hadamard=True)

@@ -52,6 +52,10 @@ LIVE_CUBE = ((20, 48, 34), (2, 8, 8))
     ("live", None, (41,), 32, {"v_format": "mxfp4"}),
     ("grouped", None, (7,), 32, {"v_format": "mxfp4"}),
     ("live", None, (50,), 32, {"cube": LIVE_CUBE}),
+    ("mid", None, (3,), 64, {"mma": "bf16"}),
+    ("live", None, (0, 55), 32, {"mma": "bf16"}),
+    ("grouped", None, (0, 39), 32, {"mma": "bf16"}),
+    ("long", True, (0,), 24, {"mma": "bf16"}),
 ])
 def test_full_size(name, expcast, heads, nrows, opts):
     w, q, k, v, plan, ec = _run(name, expcast, opts)
