@@ -13,6 +13,7 @@ VS_QK_HADAMARD = 1
 VS_V_MXFP4 = 2
 VS_OUT_BF16 = 4
 VS_BF16_MMA = 8
+VS_NOALLOC_STATS_SCRATCH_BYTES = 32 << 20
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -27,6 +28,7 @@ PROTOTYPES = {
     "vs_version": (ctypes.c_char_p, []),
     "vs_smooth_stats_workspace_bytes": (_I, [_I, _I, _I, _I, _PZ]),
     "vs_smooth_stats": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "vs_smooth_stats_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "vs_quantize_residual": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _I,
                                   _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_quantize_residual_perm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I,

@@ -18,7 +18,8 @@ from . import _abi
 from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_BF16_MMA, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
-__all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_quantize_residual",
+__all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_smooth_stats_noalloc",
+           "vs_quantize_residual",
            "vs_quantize_residual_perm", "vs_quantize_residual_ex",
            "vs_fp8_attn_fwd", "vs_fp8_attn_fwd_pcodes", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
            "vs_cube_permutation",
@@ -62,6 +63,14 @@ def vs_smooth_stats(k, v, shape, layout, k_mean, v_block_mean, v_seq_mean, ws):
                                  _p(v_block_mean), _p(v_seq_mean), _p(ws),
                                  ws.numel() * ws.element_size() if ws is not None else 0,
                                  _stream(dev)), "vs_smooth_stats")
+
+
+def vs_smooth_stats_noalloc(k, v, shape, layout, k_mean, v_block_mean, v_seq_mean):
+    B, S, H, D = shape
+    dev = _dev(k, v)
+    check(load().vs_smooth_stats_noalloc(_p(k), _p(v), B, S, H, D, layout, _p(k_mean),
+                                         _p(v_block_mean), _p(v_seq_mean), _stream(dev)),
+          "vs_smooth_stats_noalloc")
 
 
 def vs_quantize_residual(q, k, v, kv_layout, shape, softmax_scale, k_mean, v_mean, vmean_mode,

@@ -15,6 +15,8 @@
 //
 // HBM-bound: K and V are read once (4 bytes per element pair); the float64
 // adds are far below the FP64 vector rate.
+#include <mutex>
+
 #include "common.h"
 
 namespace vs {
@@ -128,10 +130,12 @@ extern "C" int vs_smooth_stats_workspace_bytes(int B, int S, int H, int D, size_
   return VS_OK;
 }
 
-extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
-                               int D, int layout, float* k_mean, float* v_block_mean,
-                               float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
-  using namespace vs;
+namespace vs {
+namespace {
+
+// Argument checks shared by both entry points (workspace excepted).
+int check_args(const uint16_t* k, const uint16_t* v, int B, int S, int H, int D, int layout,
+               const float* k_mean, const float* v_block_mean, const float* v_seq_mean) {
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (layout != VS_LAYOUT_BSHD && layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
@@ -141,15 +145,19 @@ extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int 
   if (!aligned16(k) || (v && !aligned16(v)) || (k_mean && !aligned16(k_mean)) ||
       (v_block_mean && !aligned16(v_block_mean)) || (v_seq_mean && !aligned16(v_seq_mean)))
     return VS_ERR_UNSUPPORTED;
-  const size_t need = ws_bytes_needed(B, S, H, D);
-  if (!ws || ws_bytes < need) return VS_ERR_WORKSPACE;
-  if (!aligned16(ws)) return VS_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
 
+// Both stages on a workspace of at least ws_bytes_needed() bytes.  Stage 1
+// writes every block sum it covers before stage 2 reads it, so the
+// workspace needs no clearing.
+int launch_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H, int D, int layout,
+                 float* k_mean, float* v_block_mean, float* v_seq_mean, double* ws,
+                 hipStream_t st) {
   const int nb = n_blocks(S);
-  double* ws_k = static_cast<double*>(ws);
+  double* ws_k = ws;
   double* ws_v = ws_k + static_cast<size_t>(B) * H * nb * D;
-  hipStream_t st = as_stream(stream);
   const int hfast = layout == VS_LAYOUT_BSHD && nb <= 65535;
   const dim3 g1 = hfast ? dim3(H, nb, B) : dim3(nb, H, B), g2(H, B);
   if (D == 128) {
@@ -164,4 +172,58 @@ extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int 
                        k_mean, v_seq_mean);
   }
   return launch_status();
+}
+
+// The statistics workspace of vs_smooth_stats_noalloc: one array per GPU,
+// held by the loaded library for the life of the process.  In host code the
+// name is only a stand-in for the device symbol; its device address, which
+// differs per GPU, comes from hipGetSymbolAddress once per device.
+constexpr size_t kScratchBytes = static_cast<size_t>(VS_NOALLOC_STATS_SCRATCH_BYTES);
+__device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (the current device), looked up
+// on the first call on that device; nullptr if HIP reports an error.
+double* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = static_cast<double*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace vs
+
+extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
+                               int D, int layout, float* k_mean, float* v_block_mean,
+                               float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
+  using namespace vs;
+  const int rc = check_args(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean);
+  if (rc != VS_OK || B == 0 || S == 0 || H == 0) return rc;
+  const size_t need = ws_bytes_needed(B, S, H, D);
+  if (!ws || ws_bytes < need) return VS_ERR_WORKSPACE;
+  if (!aligned16(ws)) return VS_ERR_UNSUPPORTED;
+  return launch_stats(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean,
+                      static_cast<double*>(ws), as_stream(stream));
+}
+
+extern "C" int vs_smooth_stats_noalloc(const uint16_t* k, const uint16_t* v, int B, int S,
+                                       int H, int D, int layout, float* k_mean,
+                                       float* v_block_mean, float* v_seq_mean, void* stream) {
+  using namespace vs;
+  const int rc = check_args(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean);
+  if (rc != VS_OK || B == 0 || S == 0 || H == 0) return rc;
+  if (ws_bytes_needed(B, S, H, D) > kScratchBytes) return VS_ERR_WORKSPACE;
+  double* ws = scratch_for_current_device();
+  if (!ws) return VS_ERR_HIP;
+  return launch_stats(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean, ws,
+                      as_stream(stream));
 }

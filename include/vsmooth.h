@@ -114,6 +114,33 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
                     float* v_seq_mean, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * vs_smooth_stats_noalloc -- vs_smooth_stats for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It calls no
+ * allocating routine; its workspace is a statically sized array in the
+ * library's device code, one per GPU, kept until the process ends.
+ *
+ *   arguments     as vs_smooth_stats, without ws / ws_bytes.
+ *   limit         vs_smooth_stats_workspace_bytes(B, S, H, D) must not
+ *                 exceed VS_NOALLOC_STATS_SCRATCH_BYTES (32 MiB: e.g.
+ *                 B*H = 56 heads of S = 32626 at D = 128); larger problems
+ *                 return VS_ERR_WORKSPACE before anything is launched.
+ *   device        the current HIP device (the stream's); the array's
+ *                 address on it is looked up on the first call there.
+ *                 VS_ERR_HIP if that lookup fails.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (different streams or host threads without ordering) race and give
+ * undefined results.  The kernels write every workspace entry they later
+ * read, so no call depends on what an earlier one left there.  Results are
+ * bit-identical to vs_smooth_stats.
+ */
+#define VS_NOALLOC_STATS_SCRATCH_BYTES (32u << 20)
+int vs_smooth_stats_noalloc(const uint16_t* k, const uint16_t* v, int B, int S,
+                            int H, int D, int layout, float* k_mean,
+                            float* v_block_mean, float* v_seq_mean,
+                            void* stream);
+
+/*
  * vs_quantize_residual -- per-128-token-block E4M3 quantizers for Q, centred
  * K and residual V.  Source: TeleFuser PR #40, "Changes" (centre K in FP32
  * before E4M3) and VC-Attention summary, Key Contribution 1

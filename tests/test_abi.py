@@ -78,6 +78,25 @@ def test_attn_argument_errors(lib):
     assert f(*args(S=0, D=96)) == 2
 
 
+def test_noalloc_stats_limit_is_checked_before_any_launch(lib):
+    """vs_smooth_stats_noalloc rejects a problem whose block sums exceed its
+    32 MiB array with VS_ERR_WORKSPACE, and bad arguments as vs_smooth_stats
+    does, all on the host (no GPU touched)."""
+    from bit_attention_video_smooth_amd import _abi
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.vs_smooth_stats_noalloc
+    n = ctypes.c_size_t(0)
+    assert lib.vs_smooth_stats_workspace_bytes(1, 115328, 56, 128, ctypes.byref(n)) == 0
+    assert n.value > _abi.VS_NOALLOC_STATS_SCRATCH_BYTES
+    assert f(fake, None, 1, 115328, 56, 128, 0, fake, None, None, None) == 3
+    assert lib.vs_smooth_stats_workspace_bytes(1, 32626, 56, 128, ctypes.byref(n)) == 0
+    assert n.value <= _abi.VS_NOALLOC_STATS_SCRATCH_BYTES          # the live shape fits
+    assert f(fake, None, 1, 300, 2, 96, 0, fake, None, None, None) == 2
+    assert f(fake, None, 1, 300, 2, 128, 0, fake, fake, None, None) == 1   # V mean without V
+    assert f(fake, fake, 1, 300, 2, 128, 5, fake, None, None, None) == 1   # bad layout
+    assert f(fake, fake, 1, 0, 2, 128, 0, fake, None, None, None) == 0     # empty problem
+
+
 def test_pcodes_argument_errors(lib):
     """The diagnostic entry point: a code buffer and a positive stride are
     required, MXFP4 V is not supported; all rejected on the host."""
@@ -146,6 +165,8 @@ def test_header_constants_match_the_binding():
                  "VS_V_MXFP4", "VS_OUT_BF16", "VS_BF16_MMA"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
+    m = re.search(r"#define\s+VS_NOALLOC_STATS_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _abi.VS_NOALLOC_STATS_SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("S,grid,cube", [(16, (2, 2, 4), (1, 2, 2)), (8, (1, 3, 3), (1, 2, 2)),
