@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_live_traffic.json")
 
 
-def _traffic(workload, expcast, v_format="e4m3"):
+def _traffic(workload, expcast, v_format="e4m3", mma="fp8"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     record (FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB copy), or None when the
     record is for another workload or kernel variant, or the kernel sources
@@ -37,7 +37,7 @@ def _traffic(workload, expcast, v_format="e4m3"):
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
-        if rec.get("workload") != workload or expcast or v_format != "e4m3":
+        if rec.get("workload") != workload or expcast or v_format != "e4m3" or mma != "fp8":
             return None
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -50,10 +50,26 @@ def _traffic(workload, expcast, v_format="e4m3"):
         return None
 
 
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3"):
-    """Time the oracle on one head: quantization of that head's full Q/K/V plus
-    the tiled FP8 recurrence for ``rows_n`` evenly spaced query rows over the
-    whole K/V context.  Throughput counted as 4 * rows * S * D flops."""
+    """Time the oracle (plain NumPy, float64) on one head: quantization of
+    that head's full Q/K/V plus the tiled FP8 recurrence for ``rows_n``
+    evenly spaced query rows over the whole K/V context.  Throughput counted
+    as 4 * rows * S * D flops.  ``cores`` is the number of threads the BLAS
+    library ran with (the oracle's matrix products are its only parallel
+    part); the host's logical CPU count and model are recorded next to it."""
     import workloads
     from oracle import pipeline
     try:
@@ -70,7 +86,7 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
     dt = time.perf_counter() - t0
     flops = 4.0 * len(rows) * w.S * w.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu_count": os.cpu_count(), "host_cpu_model": _cpu_model(),
             "sample": f"head 0 of {w.name} (S={w.S}, D={w.D}): full-head statistics and "
                       f"quantizers (V {v_format}{', QK Hadamard' if qk_hadamard else ''})"
                       f"{' and k-means' if w.kmeans else ''}, then the "
@@ -139,6 +155,9 @@ def main():
                     help="rotate Q and the centred K by the Hadamard matrix in the quantizers")
     ap.add_argument("--v-format", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="V residual format (mxfp4: E2M1 codes, E8M0 scale per 32 tokens)")
+    ap.add_argument("--mma", choices=["fp8", "bf16"], default="fp8",
+                    help="products on the FP8 matrix core (default) or the bf16 one "
+                         "(float32-accurate sums of the same quantized operands)")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the box's practical ceilings (library FP8/bf16 GEMMs, "
                          "device copy) and print them as one JSON line")
@@ -171,7 +190,7 @@ def main():
     q, k, v = workloads.generate(w, device=dev)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
                    fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard,
-                   v_format=args.v_format)
+                   v_format=args.v_format, mma=args.mma)
     regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
@@ -228,7 +247,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3" if args.v_format == "e4m3" else "fp8e4m3 (V: mxfp4)",
+        "dtype": ("fp8e4m3" if args.v_format == "e4m3" else "fp8e4m3 (V: mxfp4)")
+                 + ("" if args.mma == "fp8" else " operands, bf16 products"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}",
                    "kmeans": list(w.kmeans) if w.kmeans else None, "expcast": expcast,
@@ -236,6 +256,7 @@ def main():
                    "grouping_per_step": bool(w.kmeans) and regroup,
                    "qk_hadamard": bool(args.qk_hadamard),
                    "v_format": args.v_format,
+                   "products": "FP8 matrix core" if args.mma == "fp8" else "bf16 matrix core",
                    "smoothing": "K seq-mean centring + V block-mean restore",
                    "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
                    "attn_ms": round(attn_ms, 4),
@@ -244,7 +265,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(w.name, expcast, args.v_format)},
+                     "traffic": _traffic(w.name, expcast, args.v_format, args.mma)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -2,6 +2,8 @@
 
 Test infrastructure (see ``oracle/__init__``).
 
+0. optional rotary embedding of Q and K (``smoothing.rope_rows_bf16``), as
+   the model would apply it before the call;
 1. optional V-Smooth grouping: integer k-means on V, stable label sort,
    K and V permuted together (``kmeans``), or a given permutation (a static
    cube grouping, ``grouping``, or one reused from an earlier call);
@@ -38,7 +40,7 @@ def default_scale(D: int) -> np.float32:
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
                             qk_hadamard=False, v_format="e4m3", expcast=False, pcast=None,
-                            fp32=True, trace=False):
+                            fp32=True, trace=False, rope=None):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
@@ -49,6 +51,8 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     v_format: "e4m3" (per-block power-of-two scale) or "mxfp4" (E2M1 codes
     with an E8M0 scale per 32 tokens and channel, ``fp4``).  smooth: K
     centring and V mean removal on/off (off = the unsmoothed baseline).
+    rope: (cos, sin) float32 [S, D/2] tables: Q and K rotated first (token s
+    by row s of the tables, before any permutation).
     trace: also return the E4M3 probability codes of the evaluated rows
     ("p_codes", [R, S], key order of the (permuted) K) and the running max
     per tile.
@@ -58,6 +62,9 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     q = np.asarray(q, dtype=np.float32)
     k = np.asarray(k, dtype=np.float32)
     v = np.asarray(v, dtype=np.float32)
+    if rope is not None:
+        q = smoothing.rope_rows_bf16(q, *rope)
+        k = smoothing.rope_rows_bf16(k, *rope)
     S, D = q.shape
     if rows is None:
         rows = np.arange(S)

@@ -166,6 +166,42 @@ def hadamard_rows_f32(x) -> np.ndarray:
     return y
 
 
+def round_bf16(x) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to the even
+    mantissa), returned as float32: the upper 16 bits of the float32 after
+    adding 0x7FFF plus the lowest kept bit (finite inputs)."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def rope_rows_bf16(x, cos, sin) -> np.ndarray:
+    """Rotary position embedding of each row of a float32 [S, D] array of
+    bf16 values, as a model applies it to its bf16 activations: channel
+    pair i = (2i, 2i + 1) of token s is rotated by the angle whose cosine
+    and sine are cos[s, i], sin[s, i] (float32 [S, D/2]),
+
+        y_2i   = f32(f32(x_2i cos) - f32(x_2i+1 sin))
+        y_2i+1 = f32(f32(x_2i sin) + f32(x_2i+1 cos))
+
+    (each product and the sum rounded to float32), then rounded to bf16.
+
+    VC-Attention summary, Key Contribution 3: the rotary embedding is part
+    of the fused preprocessing before the quantizers.  Reading: fusing it
+    must give what the model's own rotation gives on its bf16 tensors, so
+    the result is a bf16 value -- which also keeps every statistic an exact
+    float64 sum of bf16 values.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    c = np.asarray(cos, dtype=np.float32)
+    s = np.asarray(sin, dtype=np.float32)
+    a, b = x[:, 0::2], x[:, 1::2]
+    y = np.empty_like(x)
+    y[:, 0::2] = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+    y[:, 1::2] = (a * s).astype(np.float32) + (b * c).astype(np.float32)
+    return round_bf16(y)
+
+
 def hadamard_prescale_queries(q, c) -> np.ndarray:
     """float32 (q H_D) * f32(c / D): the rotated Q in log2-score units (the
     1/D of the rotation is a power of two folded into c, one rounding)."""

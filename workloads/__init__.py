@@ -106,6 +106,34 @@ def _rope_3d(x, grid, base=10000.0, split=(44, 42, 42)):
     return out
 
 
+def rope_split(D):
+    """Channel split of the 3D rotary embedding over (t, h, w): even parts,
+    44/42/42 at D = 128 (scaled for other D)."""
+    return (44, 42, 42) if D == 128 else (D - 2 * (D // 3 // 2 * 2), D // 3 // 2 * 2, D // 3 // 2 * 2)
+
+
+def rope_tables_3d(S, D, grid, base=10000.0, split=None, device="cpu"):
+    """cos, sin float32 [S, D/2] of a 3D rotary embedding over a T x GH x GW
+    token grid in raster order (token s at (s // (GH GW), (s // GW) % GH,
+    s % GW)); pair i covers channels 2i, 2i + 1, and the pairs of each axis'
+    part of the channels rotate by position * base^(-2k / part).  Input
+    data for both the library's fused rotation and the oracle's."""
+    split = split or rope_split(D)
+    assert sum(split) == D and all(p % 2 == 0 for p in split)
+    T, GH, GW = grid
+    s = torch.arange(S, dtype=torch.float64, device=device)
+    pos = [torch.div(s, GH * GW, rounding_mode="floor"),
+           torch.remainder(torch.div(s, GW, rounding_mode="floor"), GH),
+           torch.remainder(s, GW)]
+    angs = []
+    for axis, part in enumerate(split):
+        half = part // 2
+        inv = base ** (-torch.arange(half, dtype=torch.float64, device=device) * 2.0 / part)
+        angs.append(pos[axis][:, None] * inv[None, :])
+    ang = torch.cat(angs, dim=1).to(torch.float32)
+    return torch.cos(ang).contiguous(), torch.sin(ang).contiguous()
+
+
 def _outliers(v, frac, mult, g):
     B, S, H, D = v.shape
     n = int(round(frac * S))
@@ -116,9 +144,11 @@ def _outliers(v, frac, mult, g):
     return v
 
 
-def generate(w, *, dtype=torch.bfloat16, device="cpu"):
+def generate(w, *, dtype=torch.bfloat16, device="cpu", rotate=True):
     """Return (q, k, v) tensors [B, S, H, D] of ``dtype`` on ``device`` for
-    workload w (a Workload or its name)."""
+    workload w (a Workload or its name).  rotate=False leaves the video
+    recipes' Q and K without their 3D rotary embedding (for a rotation fused
+    into the quantizers; ``rope_tables_3d`` gives its tables)."""
     if isinstance(w, str):
         w = WORKLOADS[w]
     device = torch.device(device)
@@ -140,8 +170,11 @@ def generate(w, *, dtype=torch.bfloat16, device="cpu"):
             v += e["v_off"] * rn(1, 1, H, D)
         v = _outliers(v, e["out_frac"], e["out_mult"], g)
     elif w.recipe == "rope_drift":
-        q = _rope_3d(_rms_normalize(rn(shape)), e["grid"])
-        k = _rope_3d(_rms_normalize(rn(shape)), e["grid"])
+        q = _rms_normalize(rn(shape))
+        k = _rms_normalize(rn(shape))
+        if rotate:
+            q = _rope_3d(q, e["grid"], split=rope_split(D))
+            k = _rope_3d(k, e["grid"], split=rope_split(D))
         v = rn(shape)
         amp = 0.5 + 1.5 * ru(1, 1, H, D)
         freq = 0.5 + 3.5 * ru(1, 1, H, D)
