@@ -28,13 +28,14 @@ PROTOTYPES = {
     "vs_version": (ctypes.c_char_p, []),
     "vs_smooth_stats_workspace_bytes": (_I, [_I, _I, _I, _I, _PZ]),
     "vs_smooth_stats": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "vs_smooth_stats_ex": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "vs_smooth_stats_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "vs_quantize_residual": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _I,
                                   _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_quantize_residual_perm": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I,
                                        _P, _P, _P, _P, _P, _P, _P, _P]),
-    "vs_quantize_residual_ex": (_I, [_P, _P, _P, _I, _P, _U, _I, _I, _I, _I, _F, _P, _P, _I,
-                                     _P, _P, _P, _P, _P, _P, _P, _P]),
+    "vs_quantize_residual_ex": (_I, [_P, _P, _P, _I, _P, _U, _I, _I, _I, _I, _F, _P, _P, _P,
+                                     _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "vs_fp8_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,
                              _P, _P, _P]),
     "vs_fp8_attn_fwd_pcodes": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _U,

@@ -18,7 +18,8 @@ from . import _abi
 from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_BF16_MMA, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
-__all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_smooth_stats_noalloc",
+__all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_smooth_stats_ex",
+           "vs_smooth_stats_noalloc",
            "vs_quantize_residual",
            "vs_quantize_residual_perm", "vs_quantize_residual_ex",
            "vs_fp8_attn_fwd", "vs_fp8_attn_fwd_pcodes", "vs_kmeans_workspace_bytes", "vs_kmeans_permute",
@@ -65,6 +66,16 @@ def vs_smooth_stats(k, v, shape, layout, k_mean, v_block_mean, v_seq_mean, ws):
                                  _stream(dev)), "vs_smooth_stats")
 
 
+def vs_smooth_stats_ex(k, v, shape, layout, rope_cos, rope_sin, k_mean, v_block_mean, v_seq_mean,
+                       ws):
+    B, S, H, D = shape
+    dev = _dev(k, v)
+    check(load().vs_smooth_stats_ex(_p(k), _p(v), B, S, H, D, layout, _p(rope_cos),
+                                    _p(rope_sin), _p(k_mean), _p(v_block_mean), _p(v_seq_mean),
+                                    _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                    _stream(dev)), "vs_smooth_stats_ex")
+
+
 def vs_smooth_stats_noalloc(k, v, shape, layout, k_mean, v_block_mean, v_seq_mean):
     B, S, H, D = shape
     dev = _dev(k, v)
@@ -97,11 +108,13 @@ def vs_quantize_residual_perm(q, k, v, perm, shape, softmax_scale, k_mean, v_mea
 
 
 def vs_quantize_residual_ex(q, k, v, kv_layout, perm, flags, shape, softmax_scale, k_mean, v_mean,
-                            vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu):
+                            vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
+                            rope_cos=None, rope_sin=None):
     B, S, H, D = shape
     dev = _dev(q, k, v)
     check(load().vs_quantize_residual_ex(_p(q), _p(k), _p(v), kv_layout, _p(perm), int(flags),
-                                         B, S, H, D, float(softmax_scale), _p(k_mean),
+                                         B, S, H, D, float(softmax_scale), _p(rope_cos),
+                                         _p(rope_sin), _p(k_mean),
                                          _p(v_mean), vmean_mode, _p(q8), _p(q_scale), _p(k8),
                                          _p(k_scale), _p(v8), _p(v_scale), _p(q_mu),
                                          _stream(dev)),
@@ -174,12 +187,16 @@ class Plan:
     "bf16" (VS_BF16_MMA: the quantizers write the same quantized values
     times their scales as bf16 -- q8, k8 bf16 [B,H,S_pad,D], v8 bf16
     [B,H,nb,D,128] in the bf16 PV's token order -- and both products run on
-    the bf16 matrix core, float32-accurate).
+    the bf16 matrix core, float32-accurate); rope: (cos, sin) float32
+    [S, D/2] device tables, or None: q and k are given before their rotary
+    embedding, which the statistics pass and the Q/K quantizers apply on
+    the fly (vs_smooth_stats_ex, vs_quantize_residual_ex), so the rotated
+    Q and K are never written.
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
                  kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False,
-                 v_format="e4m3", out_dtype=torch.float32, mma="fp8"):
+                 v_format="e4m3", out_dtype=torch.float32, mma="fp8", rope=None):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -222,6 +239,18 @@ class Plan:
             self.q_mu = e(B, H, S)
             self.v_mean = e(B, H, nb, D) if self.vmean_mode == VS_VMEAN_BLOCK else e(B, H, D)
             self.stats_ws = e(vs_smooth_stats_workspace_bytes(B, S, H, D), dtype=u8)
+        self.rope_cos = self.rope_sin = None
+        if rope is not None:
+            cos, sin = rope
+            for t in (cos, sin):
+                if (tuple(t.shape) != (S, D // 2) or t.dtype != torch.float32
+                        or not t.is_contiguous() or t.device != dev):
+                    raise ValueError(f"rope tables must be contiguous float32 [{S}, {D // 2}] "
+                                     "on the plan's device")
+            if kmeans is not None and not fused_gather:
+                raise ValueError("rope needs the fused gather: a gathered K copy has lost "
+                                 "the token positions its rotation angles depend on")
+            self.rope_cos, self.rope_sin = cos, sin
         self.labels = self.perm = self.k_perm = self.v_perm = self.km_ws = None
         self.cube = cube
         self._grouped = False
@@ -268,8 +297,9 @@ class Plan:
             # block means come out of the V quantizer (VS_VMEAN_BLOCK_OUT), so
             # the statistics pass reads K only; the sequence mean needs V here
             seq = self.v_mean if self.vmean_mode == VS_VMEAN_SEQ else None
-            vs_smooth_stats(kk, vv if seq is not None else None, shape, layout, self.k_mean, None,
-                            seq, self.stats_ws)
+            vs_smooth_stats_ex(kk, vv if seq is not None else None, shape, layout,
+                               self.rope_cos, self.rope_sin, self.k_mean, None, seq,
+                               self.stats_ws)
             if self.vmean_mode == VS_VMEAN_BLOCK:
                 qmode = VS_VMEAN_BLOCK_OUT
         # with a permutation and no gathered copy the quantizers read K and V
@@ -279,7 +309,7 @@ class Plan:
         vs_quantize_residual_ex(q, kk, vv, layout, perm, self.quant_flags, shape,
                                 self.softmax_scale, self.k_mean, self.v_mean, qmode, self.q8,
                                 self.q_scale, self.k8, self.k_scale, self.v8, self.v_scale,
-                                self.q_mu)
+                                self.q_mu, self.rope_cos, self.rope_sin)
         self.attn()
         return self.out, self.lse2
 

@@ -56,6 +56,30 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
   return r;
 }
 
+// float32 -> nearest bf16 (ties to the even mantissa), returned as float32
+// (finite inputs).
+__device__ __forceinline__ float round_bf16(float y) {
+  const uint32_t b = __float_as_uint(y);
+  return __uint_as_float((b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// Rotary embedding of 8 consecutive channels (4 interleaved pairs) of one
+// token, with the 4 pairs' cosines and sines: y0 = f32(f32(a cos) - f32(b sin)),
+// y1 = f32(f32(a sin) + f32(b cos)), each rounded to bf16 (what a model's own
+// rotation of its bf16 activations gives).  No contraction to FMA: every
+// product and sum is rounded on its own, in this order.
+__device__ __forceinline__ void rope8(float (&x)[8], const float4& cs, const float4& sn) {
+#pragma clang fp contract(off)
+  const float c[4] = {cs.x, cs.y, cs.z, cs.w}, s[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = x[2 * p], b = x[2 * p + 1];
+    const float ac = a * c[p], bs = b * s[p], as = a * s[p], bc = b * c[p];
+    x[2 * p] = round_bf16(ac - bs);
+    x[2 * p + 1] = round_bf16(as + bc);
+  }
+}
+
 __device__ __forceinline__ float clamp448(float x) {
   return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
 }

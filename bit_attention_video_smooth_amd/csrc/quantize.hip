@@ -75,14 +75,18 @@ __device__ __forceinline__ int src_token(const int32_t* __restrict__ perm, size_
   return s < 0 ? 0 : (s >= S ? S - 1 : s);
 }
 
-// Load TPT tokens x 8 channels of one block into float32 registers, with an
-// optional per-channel mean subtracted (one float32 subtraction).  Invalid
-// (padding) tokens are +0.
-template <int D, bool PERM>
+// Load TPT tokens x 8 channels of one block into float32 registers, rotated
+// by the rotary tables first (ROPE: row src of cos / sin, [S, D/2], pairs
+// 4c .. 4c + 3 for the thread's channels 8c .. 8c + 7), with an optional
+// per-channel mean subtracted (one float32 subtraction).  Invalid (padding)
+// tokens are +0.
+template <int D, bool PERM, bool ROPE>
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int layout, int b,
                                            int h, int j, int S, int H,
                                            const float* __restrict__ mean8,
                                            const int32_t* __restrict__ perm,
+                                           const float* __restrict__ rope_cos,
+                                           const float* __restrict__ rope_sin,
                                            float (&val)[kBlock / (256 / (D / 8))][8]) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   const int c = threadIdx.x % CH, r = threadIdx.x / CH;
@@ -106,8 +110,17 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int l
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        val[i][2 * e] = mean8 ? bf16_to_f32(ww[e] & 0xFFFFu) - mu[2 * e] : bf16_to_f32(ww[e] & 0xFFFFu);
-        val[i][2 * e + 1] = mean8 ? bf16_to_f32(ww[e] >> 16) - mu[2 * e + 1] : bf16_to_f32(ww[e] >> 16);
+        val[i][2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+        val[i][2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+      }
+      if (ROPE) {
+        const size_t t = static_cast<size_t>(src) * (D / 2) + 4 * c;
+        rope8(val[i], *reinterpret_cast<const float4*>(rope_cos + t),
+              *reinterpret_cast<const float4*>(rope_sin + t));
+      }
+      if (mean8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) val[i][e] -= mu[e];
       }
     } else {
 #pragma unroll
@@ -182,17 +195,20 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
 // token rows.  With q_mu != nullptr also q_mu[s] = c * (q_s . k_mean) from
 // the bf16 q.  PERM: rows gathered through perm (K only).  HAD: rows
 // rotated by H_D after the centring and before the scaling by pre (the
-// caller folds Q's 1/D into pre).  B16: instead of the E4M3 bytes, each
+// caller folds Q's 1/D into pre).  ROPE: rows rotated by the rotary
+// tables first (before the centring; q_mu from the rotated q).  B16:
+// instead of the E4M3 bytes, each
 // code's value times the block scale as bf16 (2 bytes per element, same
 // row layout): E4M3 values carry 4 significant bits, so the bf16 is exact
 // whenever the smallest code times the scale is a bf16 number
 // (scale >= 2^-124).
-template <int D, bool PERM, bool HAD, bool B16>
+template <int D, bool PERM, bool HAD, bool B16, bool ROPE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     const float* __restrict__ mean, float pre, uint8_t* __restrict__ codes,
     float* __restrict__ scale_out, const float* __restrict__ k_mean,
-    float* __restrict__ q_mu, float c_log2, int hfast, const int32_t* __restrict__ perm) {
+    float* __restrict__ q_mu, float c_log2, int hfast, const int32_t* __restrict__ perm,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin) {
   constexpr int CH = D / 8, ROWS = 256 / CH, TPT = kBlock / ROWS;
   __shared__ float red4[4];
   const int j = hfast ? blockIdx.y : blockIdx.x, h = hfast ? blockIdx.x : blockIdx.y,
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const float* mean8 = mean ? mean + bh * D + 8 * c : nullptr;
 
   float val[TPT][8];
-  load_block<D, PERM>(x, layout, b, h, j, S, H, mean8, perm, val);
+  load_block<D, PERM, ROPE>(x, layout, b, h, j, S, H, mean8, perm, rope_cos, rope_sin, val);
 
   if (q_mu) {
     float km[8];
@@ -594,15 +610,26 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
                   const uint16_t* k, const uint16_t* v, int kv_layout, int S, int H, int nb,
                   float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
                   float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
-                  float* q_mu, const int32_t* perm) {
+                  float* q_mu, const int32_t* perm, const float* rope_cos,
+                  const float* rope_sin) {
   const dim3 block(256);
   // with the rotation Q carries its 1/D (a power of two: exact)
   const float q_pre = HAD ? c_log2 * (1.0f / D) : c_log2;
-  hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD, B16>), gq.grid, block, 0, st, q,
-                     VS_LAYOUT_BSHD, S, H, nb, nullptr, q_pre, q8, q_scale, k_mean,
-                     k_mean ? q_mu : nullptr, c_log2, gq.hfast, nullptr);
-  hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD, B16>), gkv.grid, block, 0, st, k, kv_layout, S,
-                     H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2, gkv.hfast, perm);
+  if (rope_cos) {
+    hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD, B16, true>), gq.grid, block, 0, st, q,
+                       VS_LAYOUT_BSHD, S, H, nb, nullptr, q_pre, q8, q_scale, k_mean,
+                       k_mean ? q_mu : nullptr, c_log2, gq.hfast, nullptr, rope_cos, rope_sin);
+    hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD, B16, true>), gkv.grid, block, 0, st, k,
+                       kv_layout, S, H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2,
+                       gkv.hfast, perm, rope_cos, rope_sin);
+  } else {
+    hipLaunchKernelGGL((quant_rows_kernel<D, false, HAD, B16, false>), gq.grid, block, 0, st, q,
+                       VS_LAYOUT_BSHD, S, H, nb, nullptr, q_pre, q8, q_scale, k_mean,
+                       k_mean ? q_mu : nullptr, c_log2, gq.hfast, nullptr, nullptr, nullptr);
+    hipLaunchKernelGGL((quant_rows_kernel<D, PERM, HAD, B16, false>), gkv.grid, block, 0, st, k,
+                       kv_layout, S, H, nb, k_mean, 1.0f, k8, k_scale, nullptr, nullptr, c_log2,
+                       gkv.hfast, perm, nullptr, nullptr);
+  }
   if (vmean_mode == VS_VMEAN_BLOCK_OUT)
     hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM, FP4, B16>), gkv.grid, block, 0, st, v,
                        kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
@@ -616,7 +643,7 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
                       float softmax_scale,
                       const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
                       float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
-                      float* q_mu, void* stream) {
+                      float* q_mu, const float* rope_cos, const float* rope_sin, void* stream) {
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (perm && kv_layout != VS_LAYOUT_BSHD) return VS_ERR_INVALID_ARG;
@@ -631,7 +658,9 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   if (k_mean && !q_mu) return VS_ERR_INVALID_ARG;
   if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale)
     return VS_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, k_mean, v_mean, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm};
+  if (!rope_cos != !rope_sin) return VS_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, k_mean, v_mean, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm,
+                        rope_cos, rope_sin};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VS_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
@@ -641,7 +670,7 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   hipStream_t st = as_stream(stream);
   const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
 #define VS_QUANT_ARGS gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean, \
-    vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm
+    vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm, rope_cos, rope_sin
   const bool had = (flags & VS_QK_HADAMARD) != 0, fp4 = (flags & VS_V_MXFP4) != 0;
   const bool b16 = (flags & VS_BF16_MMA) != 0;
   // (D, permutation, rotation, FP4 V, bf16 Q/K) -> one instantiation
@@ -682,7 +711,7 @@ extern "C" int vs_quantize_residual(const uint16_t* q, const uint16_t* k, const 
                                     float* v_scale, float* q_mu, void* stream) {
   return vs::quantize_residual(q, k, v, kv_layout, nullptr, 0u, B, S, H, D, softmax_scale, k_mean,
                                v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
-                               stream);
+                               nullptr, nullptr, stream);
 }
 
 extern "C" int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -695,16 +724,17 @@ extern "C" int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k, c
   if (!perm && B > 0 && S > 0 && H > 0) return VS_ERR_INVALID_ARG;
   return vs::quantize_residual(q, k, v, VS_LAYOUT_BSHD, perm, 0u, B, S, H, D, softmax_scale, k_mean,
                                v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
-                               stream);
+                               nullptr, nullptr, stream);
 }
 
 extern "C" int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        int kv_layout, const int32_t* perm, unsigned flags, int B,
                                        int S, int H, int D, float softmax_scale,
+                                       const float* rope_cos, const float* rope_sin,
                                        const float* k_mean, float* v_mean, int vmean_mode,
                                        uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
                                        uint8_t* v8, float* v_scale, float* q_mu, void* stream) {
   return vs::quantize_residual(q, k, v, kv_layout, perm, flags, B, S, H, D, softmax_scale, k_mean,
                                v_mean, vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu,
-                               stream);
+                               rope_cos, rope_sin, stream);
 }

@@ -13,6 +13,10 @@
 //   stage 2, grid (H, B): sums the nb block sums in a fixed order and writes
 //     the sequence means.  Fixed orders make the result deterministic.
 //
+// With rotary tables (cos / sin, [S, D/2] float32, row = token) K is
+// rotated first, in the order and precision the Q/K quantizers use, so the
+// mean is that of the rotated keys the attention sees.
+//
 // HBM-bound: K and V are read once (4 bytes per element pair); the float64
 // adds are far below the FP64 vector rate.
 #include <mutex>
@@ -22,11 +26,12 @@
 namespace vs {
 namespace {
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void stats_block_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int layout,
     int S, int H, int nb, float* __restrict__ v_block_mean,
-    double* __restrict__ ws_k, double* __restrict__ ws_v, int hfast) {
+    double* __restrict__ ws_k, double* __restrict__ ws_v, int hfast,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin) {
   constexpr int CH = D / 8;           // 16-byte chunks per token row
   constexpr int ROWS = 256 / CH;      // token lanes per workgroup
   constexpr int TPT = kBlock / ROWS;  // tokens per thread
@@ -50,10 +55,21 @@ __global__ __launch_bounds__(256) void stats_block_kernel(
       const uint4 vv = v ? *reinterpret_cast<const uint4*>(v + off) : uint4{0u, 0u, 0u, 0u};
       const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sk[2 * e] += static_cast<double>(bf16_to_f32(kw[e] & 0xFFFFu));
-        sk[2 * e + 1] += static_cast<double>(bf16_to_f32(kw[e] >> 16));
+        kf[2 * e] = bf16_to_f32(kw[e] & 0xFFFFu);
+        kf[2 * e + 1] = bf16_to_f32(kw[e] >> 16);
+      }
+      if (ROPE) {
+        const size_t t = static_cast<size_t>(tok) * (D / 2) + 4 * c;
+        rope8(kf, *reinterpret_cast<const float4*>(rope_cos + t),
+              *reinterpret_cast<const float4*>(rope_sin + t));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[2 * e] += static_cast<double>(kf[2 * e]);
+        sk[2 * e + 1] += static_cast<double>(kf[2 * e + 1]);
         sv[2 * e] += static_cast<double>(bf16_to_f32(vw[e] & 0xFFFFu));
         sv[2 * e + 1] += static_cast<double>(bf16_to_f32(vw[e] >> 16));
       }
@@ -135,15 +151,18 @@ namespace {
 
 // Argument checks shared by both entry points (workspace excepted).
 int check_args(const uint16_t* k, const uint16_t* v, int B, int S, int H, int D, int layout,
-               const float* k_mean, const float* v_block_mean, const float* v_seq_mean) {
+               const float* k_mean, const float* v_block_mean, const float* v_seq_mean,
+               const float* rope_cos = nullptr, const float* rope_sin = nullptr) {
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
+  if (!rope_cos != !rope_sin) return VS_ERR_INVALID_ARG;
   if (layout != VS_LAYOUT_BSHD && layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if (!k_mean && !v_block_mean && !v_seq_mean) return VS_ERR_INVALID_ARG;
   if (!k || (!v && (v_block_mean || v_seq_mean))) return VS_ERR_INVALID_ARG;
   if (!aligned16(k) || (v && !aligned16(v)) || (k_mean && !aligned16(k_mean)) ||
-      (v_block_mean && !aligned16(v_block_mean)) || (v_seq_mean && !aligned16(v_seq_mean)))
+      (v_block_mean && !aligned16(v_block_mean)) || (v_seq_mean && !aligned16(v_seq_mean)) ||
+      (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))))
     return VS_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535) return VS_ERR_UNSUPPORTED;
   return VS_OK;
@@ -152,25 +171,34 @@ int check_args(const uint16_t* k, const uint16_t* v, int B, int S, int H, int D,
 // Both stages on a workspace of at least ws_bytes_needed() bytes.  Stage 1
 // writes every block sum it covers before stage 2 reads it, so the
 // workspace needs no clearing.
+template <int D, bool ROPE>
+void launch_stats_d(const uint16_t* k, const uint16_t* v, int S, int H, int nb, int layout,
+                    float* k_mean, float* v_block_mean, float* v_seq_mean, double* ws_k,
+                    double* ws_v, int hfast, const dim3& g1, const dim3& g2,
+                    const float* rope_cos, const float* rope_sin, hipStream_t st) {
+  hipLaunchKernelGGL((stats_block_kernel<D, ROPE>), g1, dim3(256), 0, st, k, v, layout, S, H, nb,
+                     v_block_mean, ws_k, ws_v, hfast, rope_cos, rope_sin);
+  hipLaunchKernelGGL(stats_seq_kernel<D>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb, k_mean,
+                     v_seq_mean);
+}
+
 int launch_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H, int D, int layout,
                  float* k_mean, float* v_block_mean, float* v_seq_mean, double* ws,
-                 hipStream_t st) {
+                 const float* rope_cos, const float* rope_sin, hipStream_t st) {
   const int nb = n_blocks(S);
   double* ws_k = ws;
   double* ws_v = ws_k + static_cast<size_t>(B) * H * nb * D;
   const int hfast = layout == VS_LAYOUT_BSHD && nb <= 65535;
   const dim3 g1 = hfast ? dim3(H, nb, B) : dim3(nb, H, B), g2(H, B);
+#define VS_STATS(DD, R)                                                                      \
+  launch_stats_d<DD, R>(k, v, S, H, nb, layout, k_mean, v_block_mean, v_seq_mean, ws_k, ws_v, \
+                        hfast, g1, g2, rope_cos, rope_sin, st)
   if (D == 128) {
-    hipLaunchKernelGGL(stats_block_kernel<128>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
-                       v_block_mean, ws_k, ws_v, hfast);
-    hipLaunchKernelGGL(stats_seq_kernel<128>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
-                       k_mean, v_seq_mean);
+    if (rope_cos) VS_STATS(128, true); else VS_STATS(128, false);
   } else {
-    hipLaunchKernelGGL(stats_block_kernel<64>, g1, dim3(256), 0, st, k, v, layout, S, H, nb,
-                       v_block_mean, ws_k, ws_v, hfast);
-    hipLaunchKernelGGL(stats_seq_kernel<64>, g2, dim3(1024), 0, st, ws_k, ws_v, S, H, nb,
-                       k_mean, v_seq_mean);
+    if (rope_cos) VS_STATS(64, true); else VS_STATS(64, false);
   }
+#undef VS_STATS
   return launch_status();
 }
 
@@ -202,17 +230,26 @@ double* scratch_for_current_device() {
 }  // namespace
 }  // namespace vs
 
-extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
-                               int D, int layout, float* k_mean, float* v_block_mean,
-                               float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int vs_smooth_stats_ex(const uint16_t* k, const uint16_t* v, int B, int S, int H,
+                                  int D, int layout, const float* rope_cos,
+                                  const float* rope_sin, float* k_mean, float* v_block_mean,
+                                  float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
   using namespace vs;
-  const int rc = check_args(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean);
+  const int rc =
+      check_args(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean, rope_cos, rope_sin);
   if (rc != VS_OK || B == 0 || S == 0 || H == 0) return rc;
   const size_t need = ws_bytes_needed(B, S, H, D);
   if (!ws || ws_bytes < need) return VS_ERR_WORKSPACE;
   if (!aligned16(ws)) return VS_ERR_UNSUPPORTED;
   return launch_stats(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean,
-                      static_cast<double*>(ws), as_stream(stream));
+                      static_cast<double*>(ws), rope_cos, rope_sin, as_stream(stream));
+}
+
+extern "C" int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
+                               int D, int layout, float* k_mean, float* v_block_mean,
+                               float* v_seq_mean, void* ws, size_t ws_bytes, void* stream) {
+  return vs_smooth_stats_ex(k, v, B, S, H, D, layout, nullptr, nullptr, k_mean, v_block_mean,
+                            v_seq_mean, ws, ws_bytes, stream);
 }
 
 extern "C" int vs_smooth_stats_noalloc(const uint16_t* k, const uint16_t* v, int B, int S,
@@ -224,6 +261,6 @@ extern "C" int vs_smooth_stats_noalloc(const uint16_t* k, const uint16_t* v, int
   if (ws_bytes_needed(B, S, H, D) > kScratchBytes) return VS_ERR_WORKSPACE;
   double* ws = scratch_for_current_device();
   if (!ws) return VS_ERR_HIP;
-  return launch_stats(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean, ws,
-                      as_stream(stream));
+  return launch_stats(k, v, B, S, H, D, layout, k_mean, v_block_mean, v_seq_mean, ws, nullptr,
+                      nullptr, as_stream(stream));
 }

@@ -114,6 +114,31 @@ int vs_smooth_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H,
                     float* v_seq_mean, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * vs_smooth_stats_ex -- vs_smooth_stats with the rotary embedding of K
+ * fused in: k_mean is the mean of the rotated keys, and the rotated K is
+ * never written.  Source: VC-Attention summary, Key Contribution 3 (the
+ * fused prologue absorbs the rotary embedding together with the means).
+ *
+ *   rope_cos, rope_sin  f32 [S, D/2] each, or both NULL (then this is
+ *                 vs_smooth_stats): row t holds the cosines and sines of
+ *                 token t's D/2 rotation angles; channel pair
+ *                 (2i, 2i+1) of token t turns by angle (t, i):
+ *                   y0 = a cos - b sin,  y1 = a sin + b cos,
+ *                 each product and difference / sum rounded to float32 in
+ *                 that order (no fused multiply-add), the result rounded
+ *                 to bf16 (nearest even) -- the rotation a model applies to
+ *                 its bf16 activations.  Rows are indexed by the token's
+ *                 position in k (not permuted here).  One table serves all
+ *                 B and H.  Only one of the two NULL: VS_ERR_INVALID_ARG.
+ *   all other arguments as vs_smooth_stats.  V is not rotated.
+ */
+int vs_smooth_stats_ex(const uint16_t* k, const uint16_t* v, int B, int S,
+                       int H, int D, int layout, const float* rope_cos,
+                       const float* rope_sin, float* k_mean,
+                       float* v_block_mean, float* v_seq_mean, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
  * vs_smooth_stats_noalloc -- vs_smooth_stats for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation.  It calls no
@@ -213,11 +238,23 @@ int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
                               float* v_scale, float* q_mu, void* stream);
 
 /*
- * vs_quantize_residual_ex -- the quantizers with every option: the grouping
- * permutation (as vs_quantize_residual_perm) and the QK Hadamard rotation.
- * Source: VC-Attention summary, Key Contribution 3 (the fused prologue
- * holds the gather by the permutation and a QK Hadamard rotation) and Main
+ * vs_quantize_residual_ex -- the quantizers with every option: the rotary
+ * embedding of Q and K, the grouping permutation (as
+ * vs_quantize_residual_perm) and the QK Hadamard rotation.  Source:
+ * VC-Attention summary, Key Contribution 3 (the fused prologue holds the
+ * rotary embedding, the gather by the permutation and a QK Hadamard
+ * rotation, so rotated and permuted tensors never reach HBM) and Main
  * Findings (rotating Q and K moves PSNR by at most 0.1-0.3 dB).
+ *
+ *   rope_cos, rope_sin  f32 [S, D/2] each, or both NULL: Q and K rows are
+ *                 first rotated exactly as vs_smooth_stats_ex rotates K
+ *                 (bf16 result), and everything below -- q_mu, the K
+ *                 centring, the Hadamard rotation, the block scales --
+ *                 works on the rotated rows.  K's table row is the source
+ *                 token: position i of a permuted head uses row perm[i].
+ *                 k_mean must then come from vs_smooth_stats_ex with the
+ *                 same tables.  Only one of the two NULL:
+ *                 VS_ERR_INVALID_ARG.
  *
  *   kv_layout     as vs_quantize_residual; must be VS_LAYOUT_BSHD when
  *                 perm != NULL.
@@ -252,12 +289,14 @@ int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
  *                 (block scale >= 2^-124, i.e. block amax above ~1e-35).
  *                 q_scale and k_scale are still written.
  *   all other arguments as vs_quantize_residual.
- * With perm == NULL and flags == 0 this is vs_quantize_residual.
+ * With perm, rope_cos, rope_sin == NULL and flags == 0 this is
+ * vs_quantize_residual.
  */
 int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, int kv_layout,
                             const int32_t* perm, unsigned flags, int B, int S,
                             int H, int D, float softmax_scale,
+                            const float* rope_cos, const float* rope_sin,
                             const float* k_mean, float* v_mean,
                             int vmean_mode, uint8_t* q8, float* q_scale,
                             uint8_t* k8, float* k_scale, uint8_t* v8,

@@ -143,13 +143,25 @@ def test_quant_stats_kmeans_argument_errors(lib):
               fake, fake, fake, fake, fake, fake, None, None) == 0   # empty problem
     qe = lib.vs_quantize_residual_ex
     ex = lambda **kw: [fake, fake, fake, kw.get("layout", 0), kw.get("perm", None),  # noqa: E731
-                       kw.get("flags", 0), 1, 300, 2, kw.get("D", 128), 0.1, None, None, 0,
+                       kw.get("flags", 0), 1, 300, 2, kw.get("D", 128), 0.1,
+                       kw.get("cos", None), kw.get("sin", None), None, None, 0,
                        fake, fake, fake, fake, fake, fake, None, None]
     assert qe(*ex(layout=1, perm=fake)) == 1            # a permutation needs BSHD input
     assert qe(*ex(flags=4)) == 1                        # no such flag
     assert qe(*ex(flags=16)) == 1
     assert qe(*ex(flags=8, D=96)) == 2                  # bf16 Q/K: a valid flag
     assert qe(*ex(flags=1, D=96)) == 2
+    assert qe(*ex(cos=fake)) == 1                       # rotary tables come in pairs
+    assert qe(*ex(sin=fake)) == 1
+    assert qe(*ex(cos=fake, sin=fake, D=96)) == 2
+    assert qe(*ex(cos=ctypes.c_void_p(0x1004), sin=fake)) == 2         # tables must be 16-byte aligned
+    se = lib.vs_smooth_stats_ex
+    assert se(fake, fake, 1, 300, 2, 128, 0, fake, None, fake, None, None, fake, 1 << 30,
+              None) == 1                                # rotary tables come in pairs
+    assert se(fake, fake, 1, 300, 2, 128, 0, fake, ctypes.c_void_p(0x1008), fake, None, None, fake, 1 << 30,
+              None) == 2
+    assert se(fake, fake, 1, 300, 2, 128, 0, fake, fake, fake, None, None, fake, 16, None) == 3
+    assert se(fake, fake, 1, 0, 2, 128, 0, fake, fake, fake, None, None, None, 0, None) == 0
     k = lib.vs_kmeans_permute
     assert k(fake, fake, 1, 300, 2, 128, 16, 2, fake, fake, fake, None, fake, 1 << 30, None) == 1
     assert k(fake, fake, 1, 300, 2, 128, 16, 0, fake, fake, fake, fake, fake, 1 << 30, None) == 1

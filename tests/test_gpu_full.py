@@ -22,7 +22,14 @@ def _run(name, expcast=None, opts=None):
     opts = dict(opts or {})
     print(f"[full] {name} S={w.S} H={w.H} D={w.D} kmeans={w.kmeans} expcast={expcast} "
           f"{opts}", flush=True)
-    q, k, v = workloads.generate(w, device=d)
+    rope = opts.pop("rope", False)
+    # rope: Q and K generated before their 3D rotary embedding, which the
+    # statistics pass and the quantizers apply from the tables
+    q, k, v = workloads.generate(w, device=d, rotate=not rope)
+    tables = None
+    if rope:
+        tables = workloads.rope_tables_3d(w.S, w.D, w.extra["grid"], device=d)
+        opts["rope"] = tables
     ec = w.expcast if expcast is None else expcast
     kmeans = None if "cube" in opts else w.kmeans
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, kmeans=kmeans, expcast=ec, **opts)
@@ -36,13 +43,14 @@ def _run(name, expcast=None, opts=None):
         if plan.labels is not None:
             lab_sorted = torch.gather(plan.labels, -1, plan.perm.long())
             assert bool((lab_sorted[..., 1:] >= lab_sorted[..., :-1]).all())
+    plan.tables = None if tables is None else tuple(t.cpu().numpy() for t in tables)
     return w, q, k, v, plan, ec
 
 
 LIVE_CUBE = ((20, 48, 34), (2, 8, 8))
 
 
-@pytest.mark.parametrize("name,expcast,heads,nrows,opts", [
+CASES = [
     ("mid", None, (0, 7), 64, None),
     ("live", None, (0, 27, 55), 32, None),
     ("grouped", None, (0, 39), 32, None),
@@ -56,13 +64,27 @@ LIVE_CUBE = ((20, 48, 34), (2, 8, 8))
     ("live", None, (0, 55), 32, {"mma": "bf16"}),
     ("grouped", None, (0, 39), 32, {"mma": "bf16"}),
     ("long", True, (0,), 24, {"mma": "bf16"}),
-])
+    ("live", None, (0, 27, 55), 32, {"rope": True}),
+    ("live", None, (9,), 32, {"rope": True, "mma": "bf16"}),
+    ("live", None, (20,), 32, {"rope": True, "cube": LIVE_CUBE}),
+    ("long", True, (0, 55), 24, {"rope": True}),
+]
+
+
+def _case_id(c):
+    name, expcast, _, _, opts = c
+    parts = [name] + (["expcast"] if expcast else []) + [
+        k if v is True else f"{k}_{v}" if isinstance(v, str) else k for k, v in (opts or {}).items()]
+    return "-".join(parts)
+
+
+@pytest.mark.parametrize("name,expcast,heads,nrows,opts", CASES, ids=[_case_id(c) for c in CASES])
 def test_full_size(name, expcast, heads, nrows, opts):
     w, q, k, v, plan, ec = _run(name, expcast, opts)
     rows = pipeline.sample_rows(w.S, nrows)
     opts = dict(opts or {})
     kw = {"qk_hadamard": opts.get("qk_hadamard", False),
-          "v_format": opts.get("v_format", "e4m3")}
+          "v_format": opts.get("v_format", "e4m3"), "rope": plan.tables}
     if "cube" in opts:
         from oracle import grouping
         kw["perm"] = grouping.cube_permutation(w.S, *opts["cube"])
