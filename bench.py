@@ -4,7 +4,10 @@
 
 A step is one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: (k-means grouping when the workload has it) ->
-exact K/V statistics -> per-block E4M3 quantizers -> FP8 attention.  The
+exact K/V statistics -> per-block E4M3 quantizers -> FP8 attention; on the
+video workloads Q and K arrive before their 3D rotary embedding, which the
+statistics pass and the quantizers apply on load (--rope pre: inputs
+rotated beforehand).  The
 default workload is the live DiT layer shape S=32626, H=56, D=128, B=1.
 
 Prints ONE JSON line.  ``value`` is whole-step throughput in the metric's
@@ -63,7 +66,7 @@ def _cpu_model():
     return platform.processor() or platform.machine()
 
 
-def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3"):
+def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3", rope=None):
     """Time the oracle (plain NumPy, float64) on one head: quantization of
     that head's full Q/K/V plus the tiled FP8 recurrence for ``rows_n``
     evenly spaced query rows over the whole K/V context.  Throughput counted
@@ -82,12 +85,13 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
     t0 = time.perf_counter()
     pipeline.smoothed_attention_head(qh, kh, vh, rows=rows, kmeans_kt=w.kmeans,
                                      expcast=expcast, qk_hadamard=qk_hadamard,
-                                     v_format=v_format)
+                                     v_format=v_format, rope=rope)
     dt = time.perf_counter() - t0
     flops = 4.0 * len(rows) * w.S * w.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "host_cpu_count": os.cpu_count(), "host_cpu_model": _cpu_model(),
-            "sample": f"head 0 of {w.name} (S={w.S}, D={w.D}): full-head statistics and "
+            "sample": f"head 0 of {w.name} (S={w.S}, D={w.D}): "
+                      f"{'rotary embedding, ' if rope is not None else ''}full-head statistics and "
                       f"quantizers (V {v_format}{', QK Hadamard' if qk_hadamard else ''})"
                       f"{' and k-means' if w.kmeans else ''}, then the "
                       f"tiled recurrence for {len(rows)} query rows over all {w.S} keys; "
@@ -158,6 +162,10 @@ def main():
     ap.add_argument("--mma", choices=["fp8", "bf16"], default="fp8",
                     help="products on the FP8 matrix core (default) or the bf16 one "
                          "(float32-accurate sums of the same quantized operands)")
+    ap.add_argument("--rope", choices=["fused", "pre"], default="fused",
+                    help="video workloads: Q/K given before their 3D rotary embedding, which "
+                         "the statistics pass and the quantizers apply (fused), or given "
+                         "already rotated (pre)")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the box's practical ceilings (library FP8/bf16 GEMMs, "
                          "device copy) and print them as one JSON line")
@@ -187,10 +195,13 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     expcast = w.expcast if args.expcast is None else bool(args.expcast)
     print(f"[bench] generating {w.name} S={w.S} H={w.H} D={w.D} on the GPU", file=sys.stderr, flush=True)
-    q, k, v = workloads.generate(w, device=dev)
+    rope = None
+    if "grid" in w.extra and args.rope == "fused":
+        rope = workloads.rope_tables_3d(w.S, w.D, w.extra["grid"], device=dev)
+    q, k, v = workloads.generate(w, device=dev, rotate=rope is None)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
                    fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard,
-                   v_format=args.v_format, mma=args.mma)
+                   v_format=args.v_format, mma=args.mma, rope=rope)
     regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
@@ -255,6 +266,9 @@ def main():
                    "gather": args.gather if w.kmeans else None,
                    "grouping_per_step": bool(w.kmeans) and regroup,
                    "qk_hadamard": bool(args.qk_hadamard),
+                   "rope": None if "grid" not in w.extra else
+                           ("3D, fused into statistics and quantizers" if rope is not None
+                            else "3D, applied to the inputs before the step"),
                    "v_format": args.v_format,
                    "products": "FP8 matrix core" if args.mma == "fp8" else "bf16 matrix core",
                    "smoothing": "K seq-mean centring + V block-mean restore",
@@ -269,8 +283,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        tables = None if rope is None else tuple(t.cpu().numpy() for t in rope)
         line["cpu_baseline"] = _cpu_baseline(w, q, k, v, args.cpu_rows, expcast,
-                                             args.qk_hadamard, args.v_format)
+                                             args.qk_hadamard, args.v_format, tables)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
