@@ -63,6 +63,15 @@ Probability casts (``pcast``):
   the eight mantissas M; delta ranges over [0, log2(1.5) - 1/2].  The
   "minimax centring of the one residual error term" is sigma = half that
   range, K0 = 120 - 8 sigma.  rint rounds half to even.
+* ``"mxfp4"``: a 4-bit P tile (VC-Attention summary, Future Directions,
+  first item: an on-the-fly 4-bit probability needs a per-block scale on
+  the softmax path; Main Findings: the 4-bit kernels).  Reading: the pages'
+  NVFP4 (E4M3 scale per 16) becomes gfx950's native OCP MXFP4: per query
+  row, each group of 32 consecutive keys of a tile (the MX block along the
+  PV contraction) takes the E8M0 exponent of its largest p 2^8 (the same
+  rule as the MXFP4 V residual, ``fp4.group_exponent``) and E2M1 codes of
+  p 2^8 2^-e, nearest with ties to the even code.  P~ = decode 2^(e-8).
+  The row sum stays that of the float32 p.
 * ``"none"``: no cast (P~ = p), for the exactness pins.
 
 Precision (``fp32=True``): the pages fix the exponential (and K centring) at
@@ -86,11 +95,12 @@ joint K/V permutation invariance; the exactness of the float64 score; the
 row maximum's code 0x78; lse2 independent of the E4M3 cast; constant-V and
 equal-score cases with the cast; the cast's error bound against the residual;
 the ExpCast total-variation bound of Proposition 3.1 (3.64% plus the
-underflow tail) and its two-point extremal row.
+underflow tail) and its two-point extremal row; the MXFP4 cast against a
+per-element brute force, its closed-form group cases and its error bound.
 """
 import numpy as np
 
-from . import e4m3
+from . import e4m3, fp4
 
 BLOCK = 128
 
@@ -183,6 +193,9 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
             if pcast == "e4m3":
                 codes = e4m3.encode(p8)
                 p_tilde = e4m3.decode(codes) * 2.0 ** -8
+            elif pcast == "mxfp4":
+                codes, exps, vals = mxfp4_probabilities(p8)
+                p_tilde = vals * 2.0 ** -8
             elif pcast == "none":
                 codes = None
                 p_tilde = p8 * 2.0 ** -8
@@ -208,6 +221,26 @@ def tiled_attention(q_hat, q_scale, k_hat, k_scale, v_hat, v_scale, S, c, *,
     if return_trace:
         return out, lse2, trace
     return out, lse2
+
+
+def mxfp4_probabilities(p8):
+    """MXFP4 of one tile's probabilities in units of 2^-8, p8 float [R, n]:
+    each row's keys in groups of 32 consecutive keys of the tile (the last
+    group of a ragged tile padded with zeros), per group the E8M0 exponent
+    e = fp4.group_exponent(group max) and E2M1 codes of p8 2^-e.  Returns
+    (codes uint8 [R, n], exponents int64 [R, ceil(n/32)], values float64
+    [R, n] = decode(code) 2^e)."""
+    p8 = np.asarray(p8, dtype=np.float64)
+    R, n = p8.shape
+    G = (n + fp4.GROUP - 1) // fp4.GROUP
+    pad = np.zeros((R, G * fp4.GROUP))
+    pad[:, :n] = p8
+    grp = pad.reshape(R, G, fp4.GROUP)
+    exps = fp4.group_exponents(grp.max(axis=2))
+    scale = np.exp2(exps.astype(np.float64))[..., None]
+    codes = fp4.encode(grp / scale)
+    vals = fp4.decode(codes) * scale
+    return (codes.reshape(R, -1)[:, :n], exps, vals.reshape(R, -1)[:, :n])
 
 
 def p_codes_row_major(trace, S):

@@ -74,6 +74,25 @@ def group_exponent(amax) -> int:
     return max(e, -127)
 
 
+def group_exponents(amax) -> np.ndarray:
+    """group_exponent of every entry of an array (int64, same shape)."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.zeros(a.shape, dtype=np.int64)
+    nz = a > 0
+    e[nz] = np.floor(np.log2(a[nz])).astype(np.int64) - 2
+    while True:
+        up = nz & (a > MAX_FINITE * np.exp2(e.astype(np.float64)))
+        if not up.any():
+            break
+        e[up] += 1
+    while True:
+        dn = nz & (e > -127) & (a <= MAX_FINITE * np.exp2(e.astype(np.float64) - 1))
+        if not dn.any():
+            break
+        e[dn] -= 1
+    return np.where(nz, np.maximum(e, -127), 0)
+
+
 def quantize_mxfp4(r):
     """MXFP4 codes of a float32 [S, D] residual: (codes uint8 [nb*128, D],
     exps int32 [nb*4, D]) -- group g covers tokens 32g .. 32g+31, padding

@@ -40,7 +40,7 @@ def default_scale(D: int) -> np.float32:
 def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
                             smooth=True, vmean_mode="block", kmeans_kt=None, perm=None,
                             qk_hadamard=False, v_format="e4m3", expcast=False, pcast=None,
-                            fp32=True, trace=False, rope=None):
+                            fp32=True, trace=False, rope=None, p_format="e4m3"):
     """Run the hot path on one head.
 
     q, k, v: float32 [S, D] holding bf16 values.  rows: query rows to
@@ -53,6 +53,9 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     centring and V mean removal on/off (off = the unsmoothed baseline).
     rope: (cos, sin) float32 [S, D/2] tables: Q and K rotated first (token s
     by row s of the tables, before any permutation).
+    p_format: "e4m3" (the probability tile as E4M3, or ExpCast with
+    ``expcast``) or "mxfp4" (4-bit P: E2M1 codes with an E8M0 exponent per
+    32 keys of a tile and query row, ``attention.mxfp4_probabilities``).
     trace: also return the E4M3 probability codes of the evaluated rows
     ("p_codes", [R, S], key order of the (permuted) K) and the running max
     per tile.
@@ -128,8 +131,12 @@ def smoothed_attention_head(q, k, v, *, rows=None, softmax_scale=None,
     out.update(q_codes=q_codes, q_scale=q_scale, k_codes=k_codes,
                k_scale=k_scale, v_codes=v_codes, v_scale=v_scale, q_off=q_off)
 
+    if p_format not in ("e4m3", "mxfp4"):
+        raise ValueError(f"unknown p_format {p_format!r}")
+    if p_format == "mxfp4" and (expcast or pcast not in (None, "mxfp4")):
+        raise ValueError("the 4-bit P tile is its own probability cast")
     if pcast is None:
-        pcast = "expcast" if expcast else "e4m3"
+        pcast = "mxfp4" if p_format == "mxfp4" else ("expcast" if expcast else "e4m3")
     res = attention.tiled_attention(
         e4m3.decode(q_codes[rows]), q_scale[rows // BLOCK],
         e4m3.decode(k_codes), k_scale, v_hat, v_hat_scale, S, 1.0,
