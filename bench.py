@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_live_traffic.json")
 
 
-def _traffic(workload, expcast, v_format="e4m3", mma="fp8"):
+def _traffic(workload, expcast, v_format="e4m3", mma="fp8", p_format="e4m3"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     record (FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB copy), or None when the
     record is for another workload or kernel variant, or the kernel sources
@@ -40,7 +40,8 @@ def _traffic(workload, expcast, v_format="e4m3", mma="fp8"):
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
-        if rec.get("workload") != workload or expcast or v_format != "e4m3" or mma != "fp8":
+        if (rec.get("workload") != workload or expcast or v_format != "e4m3" or mma != "fp8"
+                or p_format != "e4m3"):
             return None
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -66,7 +67,8 @@ def _cpu_model():
     return platform.processor() or platform.machine()
 
 
-def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3", rope=None):
+def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3", rope=None,
+                  p_format="e4m3"):
     """Time the oracle (plain NumPy, float64) on one head: quantization of
     that head's full Q/K/V plus the tiled FP8 recurrence for ``rows_n``
     evenly spaced query rows over the whole K/V context.  Throughput counted
@@ -85,7 +87,7 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
     t0 = time.perf_counter()
     pipeline.smoothed_attention_head(qh, kh, vh, rows=rows, kmeans_kt=w.kmeans,
                                      expcast=expcast, qk_hadamard=qk_hadamard,
-                                     v_format=v_format, rope=rope)
+                                     v_format=v_format, rope=rope, p_format=p_format)
     dt = time.perf_counter() - t0
     flops = 4.0 * len(rows) * w.S * w.D
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -162,6 +164,9 @@ def main():
     ap.add_argument("--mma", choices=["fp8", "bf16"], default="fp8",
                     help="products on the FP8 matrix core (default) or the bf16 one "
                          "(float32-accurate sums of the same quantized operands)")
+    ap.add_argument("--p-format", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="probability tile: E4M3 (default) or 4-bit (E2M1 with an E8M0 "
+                         "exponent per 32 keys)")
     ap.add_argument("--rope", choices=["fused", "pre"], default="fused",
                     help="video workloads: Q/K given before their 3D rotary embedding, which "
                          "the statistics pass and the quantizers apply (fused), or given "
@@ -201,7 +206,7 @@ def main():
     q, k, v = workloads.generate(w, device=dev, rotate=rope is None)
     plan = vs.Plan((w.B, w.S, w.H, w.D), dev, kmeans=w.kmeans, expcast=expcast,
                    fused_gather=args.gather == "fused", qk_hadamard=args.qk_hadamard,
-                   v_format=args.v_format, mma=args.mma, rope=rope)
+                   v_format=args.v_format, mma=args.mma, rope=rope, p_format=args.p_format)
     regroup = not (args.reuse_perm and w.kmeans)
     torch.cuda.synchronize(dev)
     if args.calib_copy_mib:
@@ -259,6 +264,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp8e4m3" if args.v_format == "e4m3" else "fp8e4m3 (V: mxfp4)")
+                 + ("" if args.p_format == "e4m3" else " (P: mxfp4)")
                  + ("" if args.mma == "fp8" else " operands, bf16 products"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} H={w.H} D={w.D}",
@@ -270,6 +276,7 @@ def main():
                            ("3D, fused into statistics and quantizers" if rope is not None
                             else "3D, applied to the inputs before the step"),
                    "v_format": args.v_format,
+                   "p_format": args.p_format,
                    "products": "FP8 matrix core" if args.mma == "fp8" else "bf16 matrix core",
                    "smoothing": "K seq-mean centring + V block-mean restore",
                    "pct_fp8_peak_whole_step": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
@@ -279,13 +286,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(w.name, expcast, args.v_format, args.mma)},
+                     "traffic": _traffic(w.name, expcast, args.v_format, args.mma,
+                                         args.p_format)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         tables = None if rope is None else tuple(t.cpu().numpy() for t in rope)
         line["cpu_baseline"] = _cpu_baseline(w, q, k, v, args.cpu_rows, expcast,
-                                             args.qk_hadamard, args.v_format, tables)
+                                             args.qk_hadamard, args.v_format, tables,
+                                             args.p_format)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -13,6 +13,7 @@ VS_QK_HADAMARD = 1
 VS_V_MXFP4 = 2
 VS_OUT_BF16 = 4
 VS_BF16_MMA = 8
+VS_P_MXFP4 = 16
 VS_NOALLOC_STATS_SCRATCH_BYTES = 32 << 20
 
 _P = ctypes.c_void_p

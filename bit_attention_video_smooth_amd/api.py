@@ -15,7 +15,7 @@ import math
 import torch
 
 from . import _abi
-from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_BF16_MMA, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
+from ._abi import (VS_EXPCAST, VS_OUT_BF16, VS_BF16_MMA, VS_P_MXFP4, VS_QK_HADAMARD, VS_V_MXFP4, VS_LAYOUT_BHSD, VS_LAYOUT_BSHD, VS_VMEAN_BLOCK,
                    VS_VMEAN_BLOCK_OUT, VS_VMEAN_NONE, VS_VMEAN_SEQ, check, load)
 
 __all__ = ["vs_smooth_stats_workspace_bytes", "vs_smooth_stats", "vs_smooth_stats_ex",
@@ -191,12 +191,15 @@ class Plan:
     [S, D/2] device tables, or None: q and k are given before their rotary
     embedding, which the statistics pass and the Q/K quantizers apply on
     the fly (vs_smooth_stats_ex, vs_quantize_residual_ex), so the rotated
-    Q and K are never written.
+    Q and K are never written; p_format: "e4m3" or "mxfp4" (the 4-bit
+    probability tile, VS_P_MXFP4: E2M1 P with an E8M0 exponent per 32 keys
+    of a tile; v8 then holds V's codes in token order).
     """
 
     def __init__(self, shape, device, *, softmax_scale=None, smooth=True, vmean="block",
                  kmeans=None, expcast=False, fused_gather=True, cube=None, qk_hadamard=False,
-                 v_format="e4m3", out_dtype=torch.float32, mma="fp8", rope=None):
+                 v_format="e4m3", out_dtype=torch.float32, mma="fp8", rope=None,
+                 p_format="e4m3"):
         B, S, H, D = shape
         self.shape = tuple(int(x) for x in shape)
         self.device = torch.device(device)
@@ -214,11 +217,18 @@ class Plan:
             raise ValueError(f"unknown mma {mma!r}")
         self.mma = mma
         b16 = VS_BF16_MMA if mma == "bf16" else 0
+        if p_format not in ("e4m3", "mxfp4"):
+            raise ValueError(f"unknown p_format {p_format!r}")
+        self.p_format = p_format
+        p4 = VS_P_MXFP4 if p_format == "mxfp4" else 0
+        if p4 and (expcast or v4 or b16):
+            raise ValueError("the 4-bit probability tile runs with E4M3 V on the FP8 "
+                             "matrix core, without ExpCast")
         # with the bf16 products attention takes V as bf16 values, whatever
         # format quantized them
-        self.flags = ((VS_EXPCAST if expcast else 0) | (0 if b16 else v4) | b16 |
+        self.flags = ((VS_EXPCAST if expcast else 0) | (0 if b16 else v4) | b16 | p4 |
                       (VS_OUT_BF16 if out_dtype == torch.bfloat16 else 0))
-        self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4 | b16
+        self.quant_flags = (VS_QK_HADAMARD if qk_hadamard else 0) | v4 | b16 | p4
         nb = (S + 127) // 128
         dev = self.device
         f32, u8, i32 = torch.float32, torch.uint8, torch.int32

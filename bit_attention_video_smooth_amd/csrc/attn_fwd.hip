@@ -142,6 +142,25 @@ __device__ __forceinline__ void dma16(rsrc_t rs, int voff, int soff, void* dst) 
                                            voff, soff, 0, 0);
 }
 
+// Probability casts (template parameter PC): E4M3 of 2^8 p, ExpCast-FP8,
+// or the 4-bit tile (MXFP4: E2M1 codes, one E8M0 exponent per 32 keys).
+constexpr int kPcE4m3 = 0, kPcExpcast = 1, kPcMxfp4 = 2;
+
+// First K row of QK^T sub-tile t.  With the 4-bit probability tile, A-row i
+// of sub-tile t loads key 64 (t / 2) + 16 (t % 2) + krow4(i), so that
+// register r of lane half hh holds key 64 (t / 2) + 32 hh + 16 (t % 2) + r:
+// each lane then owns 32 consecutive keys per PV k-step, one MX group.
+template <bool P4>
+constexpr int k_sub_row(int t) { return P4 ? 64 * (t >> 1) + 16 * (t & 1) : 32 * t; }
+
+__device__ __forceinline__ int krow4(int i) { return 32 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// XOR swizzle of a K row with 8 chunks under the 4-bit tile's row mapping:
+// the 16 lanes of one read then fetch rows {0-3, 4-7} + 32 {0, 1} (+ 16 or
+// 64 per sub-tile), so bit 5 of the row also enters the swizzle to keep
+// them on distinct banks.
+__device__ __forceinline__ int row_swz8_p4(int row) { return ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2); }
+
 // Bytes of one K row in LDS and HBM: D codes, or D bf16 values.
 template <int D, bool BF>
 constexpr int k_row_bytes() { return BF ? 2 * D : D; }
@@ -175,6 +194,7 @@ template <int D, bool BF>
 struct State {
   v16f s[4];
   v8i pb[BF ? 1 : 2];
+  int ps4[2];          // 4-bit tile: E8M0 byte of the lane's group per k-step
   v8bf pbf[BF ? 8 : 1];
   v16f acc[D / 32];
   v16f bias;
@@ -225,8 +245,9 @@ __device__ __forceinline__ void issue_v(const Ctx<D, BF>& c, int j, uint8_t* dst
 // lane is masked iff (valid - 4 hh - 1/2 - K) < 0, and min(s, that * inf) is
 // -inf then and s otherwise (the factor is never 0).  Compare masks would
 // each take a 64-bit scalar register pair.
+template <bool P4>
 __device__ __forceinline__ void mask_tile(v16f (&s)[4], int valid, int hh) {
-  float lim = static_cast<float>(valid - 4 * hh) - 0.5f;
+  float lim = static_cast<float>(valid - (P4 ? 32 : 4) * hh) - 0.5f;
   // opaque to the optimizer: the bound is loop-invariant where this runs
   // once, and hoisting its 64 products would only occupy registers
   asm volatile("" : "+v"(lim));
@@ -234,7 +255,8 @@ __device__ __forceinline__ void mask_tile(v16f (&s)[4], int valid, int hh) {
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float key = static_cast<float>(32 * t + 8 * (r >> 2) + (r & 3));
+      const float key = static_cast<float>(P4 ? k_sub_row<true>(t) + r
+                                              : 32 * t + 8 * (r >> 2) + (r & 3));
       s[t][r] = __builtin_fminf(s[t][r], (lim - key) * INFINITY);
     }
 }
@@ -296,10 +318,68 @@ __device__ __forceinline__ int expcast_codes4(const v16f& x, int w, float& ls) {
   return static_cast<int>(pk);
 }
 
+// The 4-bit probability tile of one lane: p8 = 2^x (float32, added to the
+// row-sum part), then per PV k-step kk the lane's 32 keys 64 kk + 32 hh ..
+// + 31 (registers r of sub-tiles 2 kk and 2 kk + 1 under the 4-bit row
+// mapping) form one MX group: e = the smallest exponent >= -127 with
+// max p8 <= 6 2^e -- from the float's bits: e = E - 2, plus 1 where the
+// mantissa exceeds 1.5 -- and the codes are E2M1(p8 2^-e), nearest with
+// ties to the even code (the conversion divides by the power of two of the
+// scale operand's exponent field; a zero field acts as 2^-127).  A 4-bit
+// operand's lane half hh holds k positions 16 hh + (0..15) in nibbles 0-15
+// and 32 + 16 hh + (0..15) in nibbles 16-31; V stores the token at
+// position p with bits 4 and 5 of p swapped, so nibble n carries key
+// 64 kk + 32 hh + n: register n % 16 of sub-tile 2 kk + n / 16.
+template <int D, bool BF>
+__device__ __forceinline__ void p_tile_mxfp4(State<D, BF>& st, float& ls) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      st.s[t][r] = __builtin_amdgcn_exp2f(st.s[t][r]);
+      ls += st.s[t][r];
+    }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, st.s[2 * kk + u][r]);
+    const uint32_t bits = __float_as_uint(mx);
+    int e = static_cast<int>(bits >> 23) - 129 + ((bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+    e = mx > 0.0f ? (e < -127 ? -127 : e) : 0;
+    const float scale = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    st.ps4[kk] = e + 127;
+    // byte k holds nibbles n = 2 k, 2 k + 1: registers r, r + 1 of sub-tile
+    // 2 kk + u, u = n / 16, r = n % 16 (the byte-select operand must be a
+    // constant)
+    auto src = [&](int k, int odd) -> float {
+      const int n = 2 * k;
+      return st.s[2 * kk + (n >> 4)][(n & 15) + odd];
+    };
+    uint32_t w[4];
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      uint32_t acc = 0u;
+      acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, src(4 * dw, 0), src(4 * dw, 1), scale, 0);
+      acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, src(4 * dw + 1, 0), src(4 * dw + 1, 1),
+                                                     scale, 1);
+      acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, src(4 * dw + 2, 0), src(4 * dw + 2, 1),
+                                                     scale, 2);
+      acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, src(4 * dw + 3, 0), src(4 * dw + 3, 1),
+                                                     scale, 3);
+      w[dw] = acc;
+    }
+    st.pb[kk] = v8i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                    static_cast<int>(w[3]), 0, 0, 0, 0};
+  }
+}
+
 // Matrix-core phase M(j) of one wave: S^T of key tile j (if j < nb), then
 // for tile j - 1 (if j >= 1) PV and the rank-one mean restore.
 //   kb: K of tile j      vb, mub: V and V mean of tile j - 1
-template <int D, bool BF, int VMEAN, bool V4>
+template <int D, bool BF, int VMEAN, bool V4, int PC>
 __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
                                            const uint8_t* kb, const uint8_t* vb,
                                            const float* mub, const uint8_t* scb) {
@@ -323,7 +403,7 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D, BF>& c, Sta
       for (int kd = 0; kd < NKS; ++kd)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint8_t* kr = kb + t * 32 * KRB;
+          const uint8_t* kr = kb + k_sub_row<PC == kPcMxfp4>(t) * KRB;
           const v8i a = make_v8i(lds_read16(kr + c.k_rd[kd][0]), lds_read16(kr + c.k_rd[kd][BF ? 0 : 1]));
           st.s[t] = mfma_fp8_scaled(a, c.qa[kd], kd == 0 ? st.bias : st.s[t], ks_e8, c.q_e8);
         }
@@ -377,6 +457,18 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D, BF>& c, Sta
         st.acc[i % DT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             a, st.pb[i / DT], st.acc[i % DT], 4, 0, 0, sa, 0, 127);
       }
+    } else if constexpr (PC == kPcMxfp4) {
+      // B = the 4-bit probability tile: lane (query, half hh) passes the 32
+      // keys 64 kk + 32 hh .. + 31 as E2M1 nibbles with their E8M0 exponent
+      v8i vf = vfrag(0);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        const v8i a = vf;
+        if (i + 1 < 2 * DT) vf = vfrag(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        st.acc[i % DT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a, st.pb[i / DT], st.acc[i % DT], 0, 4, 0, sv_e8, 0, st.ps4[i / DT]);
+      }
     } else {
       v8i vf = vfrag(0);
 #pragma unroll
@@ -425,11 +517,13 @@ __device__ __forceinline__ void phase_mfma(const int j, const Ctx<D, BF>& c, Sta
 // the running max's update where it grew, E4M3 (or ExpCast) probabilities of
 // key tile j, the tile row sum and l.  With dbg, the lane's codes are
 // written to its row of the diagnostic code buffer.
-template <int D, bool BF, bool EXPCAST>
+template <int D, bool BF, int PC>
 __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
                                            uint8_t* dbg) {
+  constexpr bool EXPCAST = PC == kPcExpcast;
   constexpr int DT = D / 32;
-  if (j == c.nb - 1 && (c.S & (kBlock - 1))) mask_tile(st.s, c.S - j * kBlock, c.hh);
+  if (j == c.nb - 1 && (c.S & (kBlock - 1)))
+    mask_tile<PC == kPcMxfp4>(st.s, c.S - j * kBlock, c.hh);
   const float xm = tile_max(st.s);   // max of s - m + 8 over the row's 128 keys
   // Tile 0 sets the reference (the bias was 0, so x = s); later tiles move
   // it where the row max grew.  tau = b - b' is the shift actually applied,
@@ -457,10 +551,15 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
   }
   float ls = 0.0f;
   int pk[16];
+  if constexpr (PC == kPcMxfp4) {
+    p_tile_mxfp4(st, ls);
+  } else {
 #pragma unroll
   for (int q = 0; q < 16; ++q)
     pk[q] = EXPCAST ? expcast_codes4(st.s[q >> 2], q & 3, ls) : p_codes4(st.s[q >> 2], q & 3, ls);
-  if constexpr (BF) {
+  }
+  if constexpr (PC == kPcMxfp4) {
+  } else if constexpr (BF) {
     // the codes' values as bf16 (exact), B operand of the bf16 PV: k-step
     // ks takes dwords 2 ks and 2 ks + 1
 #pragma unroll
@@ -483,7 +582,7 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
   }
   st.ell = ls;
   st.l += ls;
-  if (dbg) {
+  if (PC != kPcMxfp4 && dbg) {
     // dword q holds keys 32 (q / 4) + 8 (q % 4) + 4 hh .. + 3 of the tile
 #pragma unroll
     for (int q = 0; q < 16; ++q)
@@ -500,7 +599,7 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
 // last read in the other group's M(j - 1), which ended at the barrier before.
 //   kb: K_j (read)     kw: K_{j+1} (filled)
 //   vb: V_{j-1} (read) vw: V_j (filled)
-template <int D, bool BF, bool EXPCAST, int VMEAN, bool V4, bool DBG>
+template <int D, bool BF, int PC, int VMEAN, bool V4, bool DBG>
 __device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D, BF>& c, State<D, BF>& st,
                                               const uint8_t* kb, uint8_t* kw,
                                               const uint8_t* vb, uint8_t* vw,
@@ -510,14 +609,14 @@ __device__ __forceinline__ void pingpong_trip(const int j, const Ctx<D, BF>& c, 
     if (j + 1 < c.nb) issue_k<D, BF>(c, j + 1, kw);
     issue_v<D, BF, VMEAN, V4>(c, j, vw, muw, scw);
   }
-  phase_mfma<D, BF, VMEAN, V4>(j, c, st, kb, vb, mub, scb);
+  phase_mfma<D, BF, VMEAN, V4, PC>(j, c, st, kb, vb, mub, scb);
   __syncthreads();
-  if (j < c.nb) phase_valu<D, BF, EXPCAST>(j, c, st, DBG ? dbg : nullptr);
+  if (j < c.nb) phase_valu<D, BF, PC>(j, c, st, DBG ? dbg : nullptr);
   if (c.dma_wave >= 0) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 
-template <int D, bool BF, bool EXPCAST, int VMEAN, bool V4, bool DBG>
+template <int D, bool BF, int PC, int VMEAN, bool V4, bool DBG>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
@@ -599,6 +698,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
   c.vsc = v_scale + bh * nb;
 #pragma unroll
   for (int i = 0; i < (KRC == 16 ? 4 : 2); ++i) c.k_src[i] = dma_src_chunk<KRC>(lane, i) * 16;
+  if constexpr (PC == kPcMxfp4 && KRC == 8) {
+    // bit 5 of a row is bit 2 of its 1 KB block, i.e. the DMA wave's bit 0
+    // (four blocks per wave): that wave's sources flip chunk bit 2
+    if (c.dma_wave >= 0 && (c.dma_wave & 1)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) c.k_src[i] ^= 64;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < (BF ? 4 : 2); ++i)
     c.v_src[i] = dma_src_chunk<BF ? 16 : V4 ? 4 : 8>(lane, i) * 16;
@@ -611,11 +718,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
     for (int ks = 0; ks < NKS; ++ks)
       c.k_rd[ks][0] = l32 * KRB + (((2 * ks + hh) ^ row_swz<KRC>(l32)) << 4);
   } else {
+    // A-row l32 of a sub-tile: key row l32, or krow4(l32) with the 4-bit tile
+    const int krow = PC == kPcMxfp4 ? krow4(l32) : l32;
+    const int ksw = PC == kPcMxfp4 && KRC == 8 ? row_swz8_p4(krow) : row_swz<KRC>(krow);
 #pragma unroll
     for (int kd = 0; kd < NKS; ++kd)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        c.k_rd[kd][BF ? 0 : e] = l32 * KRB + (((4 * kd + 2 * hh + e) ^ row_swz<KRC>(l32)) << 4);
+        c.k_rd[kd][BF ? 0 : e] = krow * KRB + (((4 * kd + 2 * hh + e) ^ ksw) << 4);
   }
   if constexpr (BF) {
     // bf16 V rows of 256 bytes: k-step ks of lane half hh is chunk 2 ks + hh
@@ -658,10 +768,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(
 
   // ---- nb + 1 trips, two per loop iteration (static buffer roles) ----
   for (int j = 0; j <= nb; j += 2) {
-    pingpong_trip<D, BF, EXPCAST, VMEAN, V4, DBG>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0,
+    pingpong_trip<D, BF, PC, VMEAN, V4, DBG>(j, c, st, sk0, sk1, sv1, sv0, smu1, smu0,
                                                     ssc1, ssc0, dbg);
     if (j + 1 <= nb)
-      pingpong_trip<D, BF, EXPCAST, VMEAN, V4, DBG>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0,
+      pingpong_trip<D, BF, PC, VMEAN, V4, DBG>(j + 1, c, st, sk1, sk0, sv0, sv1, smu0,
                                                       smu1, ssc0, ssc1, dbg);
   }
   if (group == 0) __syncthreads();
@@ -712,11 +822,11 @@ struct Launch {
   uint8_t* dbg;
 };
 
-template <int D, bool BF, bool EXPCAST, bool V4, bool DBG>
+template <int D, bool BF, int PC, bool V4, bool DBG>
 void launch_vm(int vmean_mode, const Launch& a) {
   const dim3 grid(a.total), block(512);
 #define VS_LAUNCH(VM)                                                                             \
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF, EXPCAST, VM, V4, DBG>), grid, block, 0, a.st,     \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF, PC, VM, V4, DBG>), grid, block, 0, a.st,          \
                      a.q8, a.qs, a.k8, a.ks, a.v8, a.vs, a.vm, a.qmu, a.S, a.H, a.nb, a.npairs,    \
                      a.total, a.out, a.out_bf16, a.lse2, a.dbg, a.dbg_stride)
   if (vmean_mode == VS_VMEAN_BLOCK) VS_LAUNCH(VS_VMEAN_BLOCK);
@@ -732,12 +842,18 @@ int attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const f
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ)
     return VS_ERR_INVALID_ARG;
-  if (flags & ~(VS_EXPCAST | VS_V_MXFP4 | VS_OUT_BF16 | VS_BF16_MMA)) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_EXPCAST | VS_V_MXFP4 | VS_OUT_BF16 | VS_BF16_MMA | VS_P_MXFP4))
+    return VS_ERR_INVALID_ARG;
   if (dbg && dbg_stride < 1) return VS_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return VS_ERR_UNSUPPORTED;
   if (dbg && (flags & VS_V_MXFP4)) return VS_ERR_UNSUPPORTED;
   // the bf16 products take V as bf16 values, whatever format quantized it
   if ((flags & VS_BF16_MMA) && (flags & VS_V_MXFP4)) return VS_ERR_INVALID_ARG;
+  // the 4-bit probability tile is its own cast, on the FP8 matrix core, with
+  // E4M3 V in token order
+  if ((flags & VS_P_MXFP4) && (flags & (VS_EXPCAST | VS_V_MXFP4 | VS_BF16_MMA)))
+    return VS_ERR_INVALID_ARG;
+  if (dbg && (flags & VS_P_MXFP4)) return VS_ERR_UNSUPPORTED;
   if (B == 0 || S == 0 || H == 0) return VS_OK;
   if ((vmean_mode == VS_VMEAN_NONE) != (v_mean == nullptr)) return VS_ERR_INVALID_ARG;
   const bool qk16 = (flags & VS_BF16_MMA) != 0;
@@ -769,29 +885,36 @@ int attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const f
   a.vs = v_scale; a.vm = v_mean; a.qmu = q_mu;
   a.out = out; a.lse2 = lse2; a.dbg = dbg;
   const bool ec = (flags & VS_EXPCAST) != 0, v4 = (flags & VS_V_MXFP4) != 0;
+  const bool p4 = (flags & VS_P_MXFP4) != 0;
+  if (p4) {
+    if (D == 128) launch_vm<128, false, kPcMxfp4, false, false>(vmean_mode, a);
+    else launch_vm<64, false, kPcMxfp4, false, false>(vmean_mode, a);
+    return launch_status();
+  }
+  constexpr int E = kPcE4m3, X = kPcExpcast;
   const int sel = (D == 128 ? 8 : 0) | (qk16 ? 4 : 0) | (ec ? 2 : 0) | (v4 ? 1 : 0);
   if (dbg) {
     switch (sel) {
-      case 0: launch_vm<64, false, false, false, true>(vmean_mode, a); break;
-      case 2: launch_vm<64, false, true, false, true>(vmean_mode, a); break;
-      case 4: launch_vm<64, true, false, false, true>(vmean_mode, a); break;
-      case 6: launch_vm<64, true, true, false, true>(vmean_mode, a); break;
-      case 8: launch_vm<128, false, false, false, true>(vmean_mode, a); break;
-      case 10: launch_vm<128, false, true, false, true>(vmean_mode, a); break;
-      case 12: launch_vm<128, true, false, false, true>(vmean_mode, a); break;
-      default: launch_vm<128, true, true, false, true>(vmean_mode, a); break;
+      case 0: launch_vm<64, false, E, false, true>(vmean_mode, a); break;
+      case 2: launch_vm<64, false, X, false, true>(vmean_mode, a); break;
+      case 4: launch_vm<64, true, E, false, true>(vmean_mode, a); break;
+      case 6: launch_vm<64, true, X, false, true>(vmean_mode, a); break;
+      case 8: launch_vm<128, false, E, false, true>(vmean_mode, a); break;
+      case 10: launch_vm<128, false, X, false, true>(vmean_mode, a); break;
+      case 12: launch_vm<128, true, E, false, true>(vmean_mode, a); break;
+      default: launch_vm<128, true, X, false, true>(vmean_mode, a); break;
     }
     return launch_status();
   }
   switch (sel) {
 #define VS_A(n, d, q, e, v) case n: launch_vm<d, q, e, v, false>(vmean_mode, a); break;
-    VS_A(0, 64, false, false, false) VS_A(1, 64, false, false, true)
-    VS_A(2, 64, false, true, false) VS_A(3, 64, false, true, true)
-    VS_A(4, 64, true, false, false) VS_A(6, 64, true, true, false)
-    VS_A(8, 128, false, false, false) VS_A(9, 128, false, false, true)
-    VS_A(10, 128, false, true, false) VS_A(11, 128, false, true, true)
-    VS_A(12, 128, true, false, false)
-    default: launch_vm<128, true, true, false, false>(vmean_mode, a); break;
+    VS_A(0, 64, false, E, false) VS_A(1, 64, false, E, true)
+    VS_A(2, 64, false, X, false) VS_A(3, 64, false, X, true)
+    VS_A(4, 64, true, E, false) VS_A(6, 64, true, X, false)
+    VS_A(8, 128, false, E, false) VS_A(9, 128, false, E, true)
+    VS_A(10, 128, false, X, false) VS_A(11, 128, false, X, true)
+    VS_A(12, 128, true, E, false)
+    default: launch_vm<128, true, X, false, false>(vmean_mode, a); break;
 #undef VS_A
   }
   return launch_status();

@@ -374,6 +374,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&w)[4], uint32_t (&
 // q (low nibble first) is token 8 ((q % 16) / 4) + 4 (q / 16) + q % 4 of
 // the group -- and scale_out is u8 [B,H,nb,D,4], byte g = e + 127.
 //
+// nat (VS_P_MXFP4, E4M3 codes only): position p of a channel row holds
+// token p with bits 4 and 5 swapped -- the k order in which the attention
+// kernel's 4-bit probability tile (lane half h: k positions 16 h .. + 15
+// and 32 + 16 h .. + 15) meets V, so that each lane's 32 probabilities are
+// 32 consecutive keys.
+//
 // B16 (VS_BF16_MMA): instead of the codes, each quantized residual's value
 // (the E4M3 or E2M1 code's value times its scale, exact in bf16) as bf16,
 // per block a D x 128 tile with token tau of a channel row at position
@@ -383,7 +389,7 @@ template <int D, bool OWN_MEAN, bool PERM, bool FP4, bool B16>
 __global__ __launch_bounds__(256) void quant_vt_kernel(
     const uint16_t* __restrict__ x, int layout, int S, int H, int nb,
     float* __restrict__ v_mean, int vmean_mode, uint8_t* __restrict__ codes,
-    float* __restrict__ scale_out, int hfast, const int32_t* __restrict__ perm) {
+    float* __restrict__ scale_out, int hfast, const int32_t* __restrict__ perm, int nat) {
   constexpr int CH = D / 8;              // 8-channel groups
   constexpr int QR = 256 / CH;           // quads in flight per pass
   constexpr int NQ = kBlock / 4 / QR;    // quads per thread
@@ -582,7 +588,10 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(
     uint32_t col[8];                       // channel e: the quad's 4 tokens
     transpose4x4(lo, *reinterpret_cast<uint32_t(*)[4]>(col));
     transpose4x4(hi, *reinterpret_cast<uint32_t(*)[4]>(col + 4));
-    const int p = v_pos(4 * (a0 + QR * n));  // byte of token 4a (a multiple of 4)
+    // byte of token 4a (a multiple of 4): the FP8 MFMA token order, or (nat)
+    // the token order with bits 4 and 5 swapped
+    const int t4 = 4 * (a0 + QR * n);
+    const int p = nat ? (t4 & ~48) | (((t4 >> 4) & 1) << 5) | (((t4 >> 5) & 1) << 4) : v_pos(t4);
     const int swz = ((p >> 4) ^ (c & 7)) << 4 | (p & 15);
 #pragma unroll
     for (int e2 = 0; e2 < 8; ++e2)
@@ -611,7 +620,7 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
                   float c_log2, const float* k_mean, float* v_mean, int vmean_mode, uint8_t* q8,
                   float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
                   float* q_mu, const int32_t* perm, const float* rope_cos,
-                  const float* rope_sin) {
+                  const float* rope_sin, int nat) {
   const dim3 block(256);
   // with the rotation Q carries its 1/D (a power of two: exact)
   const float q_pre = HAD ? c_log2 * (1.0f / D) : c_log2;
@@ -632,10 +641,12 @@ void launch_quant(const BlockGrid& gq, const BlockGrid& gkv, hipStream_t st, con
   }
   if (vmean_mode == VS_VMEAN_BLOCK_OUT)
     hipLaunchKernelGGL((quant_vt_kernel<D, true, PERM, FP4, B16>), gkv.grid, block, 0, st, v,
-                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm,
+                       nat);
   else
     hipLaunchKernelGGL((quant_vt_kernel<D, false, PERM, FP4, B16>), gkv.grid, block, 0, st, v,
-                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm);
+                       kv_layout, S, H, nb, v_mean, vmean_mode, v8, v_scale, gkv.hfast, perm,
+                       nat);
 }
 
 int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, int kv_layout,
@@ -647,7 +658,9 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   if (B < 0 || S < 0 || H < 0) return VS_ERR_INVALID_ARG;
   if (kv_layout != VS_LAYOUT_BSHD && kv_layout != VS_LAYOUT_BHSD) return VS_ERR_INVALID_ARG;
   if (perm && kv_layout != VS_LAYOUT_BSHD) return VS_ERR_INVALID_ARG;
-  if (flags & ~(VS_QK_HADAMARD | VS_V_MXFP4 | VS_BF16_MMA)) return VS_ERR_INVALID_ARG;
+  if (flags & ~(VS_QK_HADAMARD | VS_V_MXFP4 | VS_BF16_MMA | VS_P_MXFP4)) return VS_ERR_INVALID_ARG;
+  // the 4-bit probability tile meets E4M3 V codes
+  if ((flags & VS_P_MXFP4) && (flags & (VS_V_MXFP4 | VS_BF16_MMA))) return VS_ERR_INVALID_ARG;
   if (vmean_mode != VS_VMEAN_NONE && vmean_mode != VS_VMEAN_BLOCK && vmean_mode != VS_VMEAN_SEQ &&
       vmean_mode != VS_VMEAN_BLOCK_OUT)
     return VS_ERR_INVALID_ARG;
@@ -670,9 +683,10 @@ int quantize_residual(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   hipStream_t st = as_stream(stream);
   const BlockGrid gq = block_grid(VS_LAYOUT_BSHD, nb, H, B), gkv = block_grid(kv_layout, nb, H, B);
 #define VS_QUANT_ARGS gq, gkv, st, q, k, v, kv_layout, S, H, nb, c_log2, k_mean, v_mean, \
-    vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm, rope_cos, rope_sin
+    vmean_mode, q8, q_scale, k8, k_scale, v8, v_scale, q_mu, perm, rope_cos, rope_sin, nat
   const bool had = (flags & VS_QK_HADAMARD) != 0, fp4 = (flags & VS_V_MXFP4) != 0;
   const bool b16 = (flags & VS_BF16_MMA) != 0;
+  const int nat = (flags & VS_P_MXFP4) != 0;
   // (D, permutation, rotation, FP4 V, bf16 Q/K) -> one instantiation
   const int sel = (D == 128 ? 16 : 0) | (b16 ? 8 : 0) | (perm ? 4 : 0) | (had ? 2 : 0) | (fp4 ? 1 : 0);
   switch (sel) {

@@ -84,6 +84,9 @@ extern "C" {
 /* vs_quantize_residual_ex and vs_fp8_attn_fwd flag */
 #define VS_BF16_MMA 8u           /* Q, K operands as scaled bf16; QK^T on the */
                                 /* bf16 matrix core (FP32-accurate scores)   */
+/* vs_quantize_residual_ex and vs_fp8_attn_fwd flag */
+#define VS_P_MXFP4 16u          /* 4-bit probability tile (E2M1, E8M0 per 32 */
+                                /* keys) and the V code order it reads       */
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* vs_status_string(int status);
@@ -281,6 +284,11 @@ int vs_quantize_residual_perm(const uint16_t* q, const uint16_t* k,
  *                 [B,H,nb,D,4], byte g = e + 127.  Source: VC-Attention
  *                 summary (V-Smooth with 4-bit operands; the pages' NVFP4
  *                 read as gfx950's MX FP4).
+ *                 | VS_P_MXFP4 (E4M3 V only): position p of each v8
+ *                 channel row holds token p with bits 4 and 5 of p swapped
+ *                 (tokens 0-15, 32-47, 16-31, 48-63 of each half-tile): the
+ *                 k order in which vs_fp8_attn_fwd's 4-bit probability tile
+ *                 meets V.
  *                 | VS_BF16_MMA: q8 and k8 receive, instead of the E4M3
  *                 bytes, each code's value times its block scale as bf16
  *                 (u16 [B,H,S_pad,D], twice the bytes): the same quantized
@@ -322,7 +330,19 @@ int vs_quantize_residual_ex(const uint16_t* q, const uint16_t* k,
  *                 then takes 4-bit V codes with their per-lane group
  *                 scales), VS_OUT_BF16, VS_BF16_MMA (q8 and k8 are the bf16
  *                 operands vs_quantize_residual_ex writes with that flag;
- *                 q_scale and k_scale are then not read and may be NULL).
+ *                 q_scale and k_scale are then not read and may be NULL),
+ *                 VS_P_MXFP4 (the 4-bit probability tile: per query row,
+ *                 each group of 32 consecutive keys of a 128-key tile gets
+ *                 the E8M0 exponent e of its largest 2^8 p -- the smallest
+ *                 e >= -127 with max <= 6 * 2^e -- and E2M1 codes of
+ *                 2^8 p 2^-e, nearest with ties to the even code, which
+ *                 the FP8/FP4 matrix core multiplies with the E4M3 V codes
+ *                 (v8 in the order vs_quantize_residual_ex writes with
+ *                 VS_P_MXFP4); l still sums the float32 p.  Not with
+ *                 VS_EXPCAST, VS_V_MXFP4 or VS_BF16_MMA: VS_ERR_INVALID_ARG.
+ *                 Source: VC-Attention summary, Future Directions (a 4-bit
+ *                 probability with its per-block scale on the softmax
+ *                 path), read as gfx950's MXFP4).
  *   out           out f32 [B,S,H,D] (bf16 [B,S,H,D] with VS_OUT_BF16: the
  *                 float32 result rounded to nearest even): attention output
  *                 in the caller's query order.
@@ -368,7 +388,7 @@ int vs_fp8_attn_fwd(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
  *                 Must not be NULL for a non-empty problem.
  *   row_stride    >= 1 (VS_ERR_INVALID_ARG otherwise).
  *   all other arguments as vs_fp8_attn_fwd (out and lse2 are written as
- *   there); VS_V_MXFP4 is VS_ERR_UNSUPPORTED here.
+ *   there); VS_V_MXFP4 and VS_P_MXFP4 are VS_ERR_UNSUPPORTED here.
  */
 int vs_fp8_attn_fwd_pcodes(const uint8_t* q8, const float* q_scale,
                            const uint8_t* k8, const float* k_scale,

@@ -35,12 +35,19 @@ def v16_rows(v16_head):
     return out
 
 
-def v8_rows(v8_head):
+# token held at position p of a V block row for the 4-bit probability tile
+# (VS_P_MXFP4): bits 4 and 5 of p swapped
+P4_TOKEN_OF_POS = np.array([(p & ~48) | (((p >> 4) & 1) << 5) | (((p >> 5) & 1) << 4)
+                            for p in range(128)])
+
+
+def v8_rows(v8_head, token_of_pos=None):
     """[nb, D, 128] block-transposed V codes -> [nb*128, D] in token order."""
+    order = V_TOKEN_OF_POS if token_of_pos is None else token_of_pos
     nb, D, _ = v8_head.shape
     out = np.zeros((nb * 128, D), dtype=np.uint8)
     for j in range(nb):
-        out[j * 128 + V_TOKEN_OF_POS, :] = v8_head[j].T
+        out[j * 128 + order, :] = v8_head[j].T
     return out
 
 
@@ -127,6 +134,10 @@ def plan_head(plan, b, h, rows):
     elif getattr(plan, "v_format", "e4m3") == "mxfp4":
         out["v_codes"], out["v_exps"] = v4_rows(g(plan.v8), g(plan.v_scale))
         out["v_scale"] = None
+    elif getattr(plan, "p_format", "e4m3") == "mxfp4":
+        # the 4-bit probability tile's V layout: position p holds token p with
+        # bits 4 and 5 swapped
+        out["v_codes"] = v8_rows(g(plan.v8), P4_TOKEN_OF_POS)
     else:
         out["v_codes"] = v8_rows(g(plan.v8))
     if plan.labels is not None:

@@ -69,7 +69,11 @@ def test_attn_argument_errors(lib):
     assert f(*args(B=-1)) == 1
     assert f(*args(mode=1)) == 1                      # block mean without a buffer
     assert f(*args(mode=7, vm=fake)) == 1
-    assert f(*args(flags=16)) == 1
+    assert f(*args(flags=32)) == 1
+    assert f(*args(flags=16 | 1)) == 1                 # 4-bit P with ExpCast
+    assert f(*args(flags=16 | 2)) == 1                 # 4-bit P with MXFP4 V
+    assert f(*args(flags=16 | 8)) == 1                 # 4-bit P with bf16 products
+    assert f(*args(flags=16, D=96)) == 2               # 4-bit P: a valid flag
     assert f(*args(flags=4, D=96)) == 2                # bf16 output: a valid flag
     assert f(*args(flags=8, D=96)) == 2                # bf16 QK operands: a valid flag
     assert f(*args(flags=3, D=96)) == 2                # ExpCast with MXFP4 V: a valid flag pair
@@ -108,6 +112,7 @@ def test_pcodes_argument_errors(lib):
     assert f(*args(codes=None)) == 1
     assert f(*args(stride=0)) == 1
     assert f(*args(flags=2)) == 2
+    assert f(*args(flags=16)) == 2                       # no code buffer for 4-bit P
     assert f(*args(D=96)) == 2
 
 
@@ -148,7 +153,10 @@ def test_quant_stats_kmeans_argument_errors(lib):
                        fake, fake, fake, fake, fake, fake, None, None]
     assert qe(*ex(layout=1, perm=fake)) == 1            # a permutation needs BSHD input
     assert qe(*ex(flags=4)) == 1                        # no such flag
-    assert qe(*ex(flags=16)) == 1
+    assert qe(*ex(flags=32)) == 1
+    assert qe(*ex(flags=16 | 2)) == 1                   # token-order V is E4M3 only
+    assert qe(*ex(flags=16 | 8)) == 1
+    assert qe(*ex(flags=16, D=96)) == 2                 # 4-bit P's V layout: a valid flag
     assert qe(*ex(flags=8, D=96)) == 2                  # bf16 Q/K: a valid flag
     assert qe(*ex(flags=1, D=96)) == 2
     assert qe(*ex(cos=fake)) == 1                       # rotary tables come in pairs
@@ -174,7 +182,7 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     for name in ["VS_VMEAN_NONE", "VS_VMEAN_BLOCK", "VS_VMEAN_SEQ", "VS_VMEAN_BLOCK_OUT",
                  "VS_LAYOUT_BSHD", "VS_LAYOUT_BHSD", "VS_EXPCAST", "VS_QK_HADAMARD",
-                 "VS_V_MXFP4", "VS_OUT_BF16", "VS_BF16_MMA"]:
+                 "VS_V_MXFP4", "VS_OUT_BF16", "VS_BF16_MMA", "VS_P_MXFP4"]:
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_abi, name), name
     m = re.search(r"#define\s+VS_NOALLOC_STATS_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
