@@ -174,7 +174,7 @@ def main():
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the box's practical ceilings (library FP8/bf16 GEMMs, "
                          "device copy) and print them as one JSON line")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a known-size "

@@ -3,8 +3,8 @@
 // VC-Attention summary (Key Contribution 1, "Methodology in Plain English"):
 // tokens are grouped by a lightweight online k-means over the value tokens,
 // the labels are sorted into a permutation and K and V are permuted together
-// by it; attention is unchanged because permuting keys permutes the columns
-// of the probability matrix exactly as the rows of V.
+// by it; attention is unchanged since the one reordering moves the columns
+// of the probability matrix and the rows of V alike.
 //
 // The grouping is an integer computation (see vsmooth.h), so labels and the
 // permutation are the same on every run and every implementation:

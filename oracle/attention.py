@@ -56,13 +56,13 @@ Probability casts (``pcast``):
   Methodology): the E4M3 byte is an affine function of log2 of its value, so
   the code is formed from the log-domain score by one multiply-add and one
   integer conversion:  code = rint(8 (s - m') + K0), codes below 8 (the
-  subnormals) become 0 ("maps underflow to zero"), codes above 126 are
-  clipped ("keeps codes in the normal E4M3 range"), and the byte is used as
-  an E4M3 value as is.  With the same 2^8 offset, an exact mapping would be
+  subnormals) become 0 (underflow maps to zero), codes above 126 are
+  clipped (the codes stay in the normal E4M3 range), and the byte is used
+  as an E4M3 value as is.  With the same 2^8 offset, an exact mapping would be
   code = 8 log2(p) + 120 - 8 delta(M), delta(M) = log2(1 + M/8) - M/8 over
-  the eight mantissas M; delta ranges over [0, log2(1.5) - 1/2].  The
-  "minimax centring of the one residual error term" is sigma = half that
-  range, K0 = 120 - 8 sigma.  rint rounds half to even.
+  the eight mantissas M; delta ranges over [0, log2(1.5) - 1/2].  The pages
+  centre that one remaining error term minimax: sigma = half that range,
+  K0 = 120 - 8 sigma.  rint rounds half to even.
 * ``"mxfp4"``: a 4-bit P tile (VC-Attention summary, Future Directions,
   first item: an on-the-fly 4-bit probability needs a per-block scale on
   the softmax path; Main Findings: the 4-bit kernels).  Reading: the pages'

@@ -4,9 +4,9 @@ Test infrastructure (see ``oracle/__init__``).
 
 The pages say tokens are grouped by a lightweight online k-means over the
 value tokens of a head, the labels are sorted into a permutation, and keys and
-values are permuted together by it, which leaves attention unchanged because
-permuting keys permutes the columns of the probability matrix exactly as it
-permutes the rows of V (VC-Attention summary, Key Contribution 1 and
+values are permuted together by it, which leaves attention unchanged: the
+same reordering hits the columns of the probability matrix and the rows of
+V, and their product does not see it (VC-Attention summary, Key Contribution 1 and
 "Methodology in Plain English").  They fix neither the precision, the
 initialisation nor the tie rules.  The reading used here makes the grouping an
 integer computation, so that any implementation of it gets the same labels:

@@ -16,8 +16,9 @@ Test infrastructure (see ``oracle/__init__``).
    (``attention``).
 
 Q, O and lse2 stay in the original token order; only K and V are permuted
-(VC-Attention summary, Methodology: permuting keys permutes the columns of
-the probability matrix exactly as the rows of V).
+(VC-Attention summary, Methodology: one reordering applied to the keys and
+the values reorders the probability matrix's columns and V's rows alike,
+which leaves their product unchanged).
 
 parity unpinned: the end result (O, lse2) of the quantized pipeline is not
 pinned beyond the oracle itself, because the pages print no worked example

@@ -19,8 +19,8 @@ Sources
   "Methodology in Plain English").  The sequence-mean variant is TeleFuser's
   "centralize V, restore its sequence mean after attention".
 * Block quantization scale: one scale per block set by the block's largest
-  entry (VC-Attention abstract: "a block's quantization scale is set by its
-  largest entries").  Reading, for Q, centred K and the V residual alike:
+  entry (VC-Attention abstract: the largest entries of a block decide its
+  scale).  Reading, for Q, centred K and the V residual alike:
   the scale is the power of two 2^e with e the smallest integer such that
   amax <= 448 * 2^e over the block's valid tokens and all channels (e >=
   -126; e = 0 when amax == 0), and codes = E4M3(x * 2^-e), round to nearest
