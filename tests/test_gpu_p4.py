@@ -114,3 +114,36 @@ def test_four_bit_probabilities_live_full_size():
         check_intermediates(got, ref, w.S, label=f"p4 live h{h}")
         e = check_attn(got["O"], got["lse2"], ref, label=f"p4 live h{h}", strict=False)
         assert e["lse2"] <= TOL_LSE2, e
+
+
+@pytest.mark.parametrize("opt", ["kmeans", "cube", "hadamard", "rope"])
+def test_four_bit_probabilities_with_prologue_options(opt):
+    """The 4-bit tile behind the other prologue options (k-means and cube
+    permutations read V through the permutation into the 4-bit tile's V
+    order; the QK Hadamard rotation and the rotary embedding change only
+    Q and K): codes bit-exact, O and lse2 as above."""
+    from oracle import grouping
+    w = SMALL
+    print(f"[p4 options] {opt}", flush=True)
+    q, k, v = workloads.generate(w)
+    kw, okw = {}, {}
+    if opt == "kmeans":
+        kw["kmeans"] = okw["kmeans_kt"] = (8, 3)
+    elif opt == "cube":
+        cube = ((1, 20, 30), (1, 4, 4))
+        kw["cube"] = cube
+        okw["perm"] = grouping.cube_permutation(w.S, *cube)
+    elif opt == "hadamard":
+        kw["qk_hadamard"] = okw["qk_hadamard"] = True
+    else:
+        cos, sin = workloads.rope_tables_3d(w.S, w.D, (1, 20, 30))
+        kw["rope"] = (cos.to(dev()), sin.to(dev()))
+        okw["rope"] = (cos.numpy(), sin.numpy())
+    plan = run_plan(q, k, v, p_format="mxfp4", **kw)
+    rows = np.arange(w.S)
+    for h in range(w.H):
+        ref = oracle_head(q, k, v, 0, h, rows, p_format="mxfp4", **okw)
+        got = plan_head(plan, 0, h, rows)
+        check_intermediates(got, ref, w.S, label=f"p4 {opt} h{h}")
+        e = check_attn(got["O"], got["lse2"], ref, label=f"p4 {opt} h{h}", strict=False)
+        assert e["lse2"] <= TOL_LSE2, e
