@@ -147,3 +147,24 @@ def test_four_bit_probabilities_with_prologue_options(opt):
         check_intermediates(got, ref, w.S, label=f"p4 {opt} h{h}")
         e = check_attn(got["O"], got["lse2"], ref, label=f"p4 {opt} h{h}", strict=False)
         assert e["lse2"] <= TOL_LSE2, e
+
+
+@pytest.mark.parametrize("S", [1, 7, 31, 33, 128, 129, 300])
+@pytest.mark.parametrize("D", [64, 128])
+def test_four_bit_probabilities_ragged_shapes(S, D):
+    """Ragged and tiny sequences: masked keys of the last tile fall inside
+    and across the 32-key groups (S = 1, 31, 33 ...), B = 2, three heads."""
+    w = workloads.Workload("rag4", 2, S, 3, D, 200 + S + D, "offsets",
+                           extra=dict(k_off=2.0, k_off_shared=False, v_off=1.0,
+                                      out_frac=0.01, out_mult=10.0))
+    q, k, v = workloads.generate(w)
+    plan = run_plan(q, k, v, p_format="mxfp4")
+    rows = np.arange(S)
+    for b in range(2):
+        for h in range(3):
+            ref = oracle_head(q, k, v, b, h, rows, p_format="mxfp4")
+            got = plan_head(plan, b, h, rows)
+            check_intermediates(got, ref, S, label=f"p4 S{S} D{D} b{b} h{h}")
+            e = check_attn(got["O"], got["lse2"], ref, label=f"p4 S{S} D{D} b{b} h{h}",
+                           strict=False)
+            assert e["lse2"] <= TOL_LSE2, e
