@@ -13,11 +13,19 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,opts", [("tiny", {}), ("mid", {"kmeans": (16, 3)}),
-                                       ("mid", {"v_format": "mxfp4", "expcast": True})])
+                                       ("mid", {"v_format": "mxfp4", "expcast": True}),
+                                       ("mid", {"p_format": "mxfp4", "rope": True}),
+                                       ("mid", {"mma": "bf16", "cube": True})])
 def test_graph_replays_equal_eager(name, opts):
     import bit_attention_video_smooth_amd as vs
     w = workloads.WORKLOADS[name]
     d = dev()
+    opts = dict(opts)
+    if opts.pop("rope", False):
+        # a 3D rotary table over an 8 x 32 x 32 token grid (S = 8192)
+        opts["rope"] = workloads.rope_tables_3d(w.S, w.D, (8, 32, 32), device=d)
+    if opts.pop("cube", False):
+        opts["cube"] = ((8, 32, 32), (2, 8, 8))
     q, k, v = (t.to(d) for t in workloads.generate(w))
     q2, k2, v2 = (t.flip(1).contiguous() for t in (q, k, v))     # other inputs
     plan = vs.Plan((w.B, w.S, w.H, w.D), d, **opts)
