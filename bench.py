@@ -100,6 +100,45 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
                       f"{dt:.1f} s wall; flops counted 4*rows*S*D"}
 
 
+def _mfma_loop_rates(dev, timed):
+    """The matrix core on its own: libvsmooth_peak.so's loop of independent
+    FP8 (32x32x64) or bf16 (32x32x16) products on register operands, one
+    wave per SIMD.  Returns TFLOP/s, the shader clock (s_memtime ticks over
+    event time) and the matrix core's cycles per product."""
+    import ctypes
+    import torch
+    from bit_attention_video_smooth_amd.build import PEAK_LIB
+
+    if not os.path.exists(PEAK_LIB):
+        return {"mfma_loop": "libvsmooth_peak.so not built"}
+    lib = ctypes.CDLL(PEAK_LIB)
+    fn = lib.vs_peak_mfma_loop
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    out = {}
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for kind, name, flops in ((0, "fp8", 2 * 32 * 32 * 64), (1, "bf16", 2 * 32 * 32 * 16)):
+        # one workgroup of four waves per CU: one wave per SIMD, all resident
+        for threads, blocks in ((256, 256),):
+            iters = 40000 if kind == 0 else 80000
+            waves = blocks * threads // 64
+            ticks = torch.zeros(waves, dtype=torch.int64, device=dev)
+            sink = torch.zeros(waves, dtype=torch.float32, device=dev)
+
+            def run():
+                rc = fn(kind, blocks, threads, iters, ctypes.c_void_p(ticks.data_ptr()),
+                        ctypes.c_void_p(sink.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"vs_peak_mfma_loop returned {rc}")
+            t = timed(run, n=5)
+            tk = float(ticks.double().mean().item())      # each wave's loop, shader cycles
+            per_simd = waves // 1024
+            out[f"{name}_mfma_loop_{per_simd}w_tflops"] = round(waves * iters * 8 * flops / t / 1e12, 1)
+            out[f"{name}_mfma_loop_{per_simd}w_clock_ghz"] = round(tk / t / 1e9, 3)
+            out[f"{name}_mfma_loop_{per_simd}w_cycles_per_product"] = round(tk / (iters * 8 * per_simd), 1)
+    return out
+
+
 def _peaks(dev):
     """Practical ceilings on this machine next to the published peaks: the
     vendor library's dense FP8 (E4M3) and bf16 GEMMs (torch._scaled_mm /
@@ -135,6 +174,7 @@ def _peaks(dev):
         t = timed(lambda: torch.matmul(x, y))
         out[f"bf16_gemm_{n}_tflops"] = round(2.0 * n ** 3 / t / 1e12, 1)
         del a, b, x, y
+    out.update(_mfma_loop_rates(dev, timed))
     src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     t = timed(lambda: dst.copy_(src), n=10)

@@ -4,6 +4,8 @@
 
 Each .hip source compiles to an object in parallel, then one shared library
 is linked.  Packed-FP32 instruction forms are disabled for all device code.
+The matrix-core rate microbenchmark (csrc/mfma_peak.hip, used by bench.py
+--peaks only) links into its own libvsmooth_peak.so.
 """
 import concurrent.futures
 import os
@@ -18,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvsmooth.so")
 SOURCES = ["status.hip", "smooth_stats.hip", "quantize.hip", "attn_fwd.hip", "kmeans.hip",
            "grouping.hip"]
+PEAK_SOURCE = "mfma_peak.hip"
+PEAK_LIB = os.path.join(HERE, "libvsmooth_peak.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -39,15 +43,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(_compile, SOURCES, objs))
+    srcs = SOURCES + [PEAK_SOURCE]
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        list(ex.map(_compile, srcs, objs))
+    peak_obj = objs.pop()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, peak_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PEAK_LIB)
     shutil.rmtree(objdir, ignore_errors=True)
     if verbose:
         print(f"built {LIB}")
