@@ -101,30 +101,33 @@ __global__ __launch_bounds__(256) void stats_block_kernel(
   }
 }
 
-// One workgroup per (b, h): G = 1024 / D groups of D threads each sum a
-// strided subset of the block sums, then group 0 adds the G partials in order.
+// One workgroup per (b, h, 32-channel slice): G = 32 groups of 32 threads
+// each sum a strided subset of the block sums of the slice's channels, then
+// group 0 adds the G partials in order.  The float64 sums of bf16 values
+// are exact, so the result does not depend on the split.
 template <int D>
 __global__ __launch_bounds__(1024) void stats_seq_kernel(
     const double* __restrict__ ws_k, const double* __restrict__ ws_v, int S,
     int H, int nb, float* __restrict__ k_mean, float* __restrict__ v_seq_mean) {
-  constexpr int G = 1024 / D;
-  __shared__ double part[2][G][D];
+  constexpr int C = 32, G = 1024 / C;
+  __shared__ double part[2][G][C];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int d = threadIdx.x % D, g = threadIdx.x / D;
+  const int c = threadIdx.x % C, g = threadIdx.x / C;
+  const int d = blockIdx.z * C + c;
   const size_t base = (static_cast<size_t>(b) * H + h) * nb * D;
   double sk = 0.0, sv = 0.0;
   for (int j = g; j < nb; j += G) {
     sk += ws_k[base + static_cast<size_t>(j) * D + d];
     if (v_seq_mean) sv += ws_v[base + static_cast<size_t>(j) * D + d];
   }
-  part[0][g][d] = sk;
-  part[1][g][d] = sv;
+  part[0][g][c] = sk;
+  part[1][g][c] = sv;
   __syncthreads();
   if (g == 0) {
     double tk = 0.0, tv = 0.0;
     for (int gg = 0; gg < G; ++gg) {
-      tk += part[0][gg][d];
-      tv += part[1][gg][d];
+      tk += part[0][gg][c];
+      tv += part[1][gg][c];
     }
     const size_t o = (static_cast<size_t>(b) * H + h) * D + d;
     if (k_mean) k_mean[o] = static_cast<float>(tk / static_cast<double>(S));
@@ -189,7 +192,7 @@ int launch_stats(const uint16_t* k, const uint16_t* v, int B, int S, int H, int 
   double* ws_k = ws;
   double* ws_v = ws_k + static_cast<size_t>(B) * H * nb * D;
   const int hfast = layout == VS_LAYOUT_BSHD && nb <= 65535;
-  const dim3 g1 = hfast ? dim3(H, nb, B) : dim3(nb, H, B), g2(H, B);
+  const dim3 g1 = hfast ? dim3(H, nb, B) : dim3(nb, H, B), g2(H, B, D / 32);
 #define VS_STATS(DD, R)                                                                      \
   launch_stats_d<DD, R>(k, v, S, H, nb, layout, k_mean, v_block_mean, v_seq_mean, ws_k, ws_v, \
                         hfast, g1, g2, rope_cos, rope_sin, st)
