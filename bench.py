@@ -100,11 +100,26 @@ def _cpu_baseline(w, q, k, v, rows_n, expcast, qk_hadamard=False, v_format="e4m3
                       f"{dt:.1f} s wall; flops counted 4*rows*S*D"}
 
 
+def _settle(run, dev, seconds=0.3):
+    """Back-to-back launches for `seconds`, so that the clock reached under
+    sustained load (power management reacts over tens of milliseconds) is
+    what the timed launches see."""
+    import time
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(4):
+            run()
+        torch.cuda.synchronize(dev)
+
+
 def _mfma_loop_rates(dev, timed):
     """The matrix core on its own: libvsmooth_peak.so's loop of independent
-    FP8 (32x32x64) or bf16 (32x32x16) products on register operands, one
-    wave per SIMD.  Returns TFLOP/s, the shader clock (s_memtime ticks over
-    event time) and the matrix core's cycles per product."""
+    FP8 (32x32x64) or bf16 (32x32x16) products on register operands (random
+    operand bytes, different for each of the eight accumulators), one wave
+    per SIMD, timed after 0.3 s of sustained load.  Returns TFLOP/s, the
+    shader clock (s_memtime ticks over event time) and the matrix core's
+    cycles per product."""
     import ctypes
     import torch
     from bit_attention_video_smooth_amd.build import PEAK_LIB
@@ -130,12 +145,67 @@ def _mfma_loop_rates(dev, timed):
                         ctypes.c_void_p(sink.data_ptr()), stream)
                 if rc != 0:
                     raise RuntimeError(f"vs_peak_mfma_loop returned {rc}")
+            _settle(run, dev)
             t = timed(run, n=5)
             tk = float(ticks.double().mean().item())      # each wave's loop, shader cycles
             per_simd = waves // 1024
             out[f"{name}_mfma_loop_{per_simd}w_tflops"] = round(waves * iters * 8 * flops / t / 1e12, 1)
             out[f"{name}_mfma_loop_{per_simd}w_clock_ghz"] = round(tk / t / 1e9, 3)
             out[f"{name}_mfma_loop_{per_simd}w_cycles_per_product"] = round(tk / (iters * 8 * per_simd), 1)
+    return out
+
+
+def _mix_loop_clocks(dev):
+    """The clock each phase mix of the attention kernel holds under sustained
+    load (libvsmooth_peak.so's vs_peak_mix_loop, eight waves per CU): FP8
+    products with register operands, the same products with their A operand
+    read from LDS (2 KB per product, as in the matrix-core phase), the vector
+    phase's mix (max3 chain, exp2, E4M3 packs, row-sum adds), and products
+    from LDS co-running with the vector mix on every SIMD; random operand
+    bytes, the last launch after 0.3 s of sustained load.  Each wave's
+    clock is its s_memtime ticks over its s_memrealtime (100 MHz) ticks."""
+    import ctypes
+    import torch
+    from bit_attention_video_smooth_amd.build import PEAK_LIB
+
+    if not os.path.exists(PEAK_LIB):
+        return {"mix_loop": "libvsmooth_peak.so not built"}
+    lib = ctypes.CDLL(PEAK_LIB)
+    fn = lib.vs_peak_mix_loop
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 4
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    blocks = 256                        # one workgroup of eight waves per CU
+    n = blocks * 8
+    ticks = torch.zeros(n, dtype=torch.int64, device=dev)
+    rticks = torch.zeros(n, dtype=torch.int64, device=dev)
+    sink = torch.zeros(n, dtype=torch.float32, device=dev)
+    out = {}
+    for kind, name in ((3, "products_reg"), (0, "products_lds"), (1, "vector_mix"),
+                       (2, "products_lds+vector_mix")):
+        iters_p, iters_v = 20000, 8000
+
+        def run():
+            rc = fn(kind, blocks, iters_p, iters_v, ctypes.c_void_p(ticks.data_ptr()),
+                    ctypes.c_void_p(rticks.data_ptr()), ctypes.c_void_p(sink.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"vs_peak_mix_loop returned {rc}")
+        _settle(run, dev)
+        torch.cuda.synchronize(dev)
+        tk = ticks.double().cpu()
+        rt = rticks.double().cpu()
+        wave_in_wg = torch.arange(n) % 8
+        if kind == 2:
+            roles = (("_products", wave_in_wg < 4, iters_p), ("_vector", wave_in_wg >= 4, iters_v))
+        else:
+            roles = (("", wave_in_wg >= 0, iters_v if kind == 1 else iters_p),)
+        for suffix, sel, it in roles:
+            out[f"mix_{name}{suffix}_clock_ghz"] = round((tk[sel] / rt[sel] * 0.1).median().item(), 3)
+            out[f"mix_{name}{suffix}_cycles_per_turn"] = round(tk[sel].median().item() / it, 1)
+        if kind in (0, 3):
+            # every wave's eight products per turn over the slowest wave's time
+            secs = rt.max().item() / 1e8
+            out[f"mix_{name}_tflops"] = round(n * iters_p * 8 * 2 * 32 * 32 * 64 / secs / 1e12, 1)
     return out
 
 
@@ -175,6 +245,7 @@ def _peaks(dev):
         out[f"bf16_gemm_{n}_tflops"] = round(2.0 * n ** 3 / t / 1e12, 1)
         del a, b, x, y
     out.update(_mfma_loop_rates(dev, timed))
+    out.update(_mix_loop_clocks(dev))
     src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     t = timed(lambda: dst.copy_(src), n=10)
