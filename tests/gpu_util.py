@@ -184,15 +184,20 @@ def check_intermediates(gpu, ref, S, label=""):
         np.testing.assert_array_equal(gpu["perm"], ref["perm"], err_msg=label + " perm")
 
 
-def pcode_flips(gpu_codes, ref_codes, label=""):
+def pcode_flips(gpu_codes, ref_codes, label="", expcast=False):
     """Compare the kernel's E4M3 probability codes ([R, S], from
     Plan.attn_pcodes) with the oracle's: returns per-row counts of differing
     codes, and checks that each differs by one code step (a rounding boundary
-    crossed, not a wrong value)."""
+    crossed, not a wrong value).  Steps count the codes the cast can produce:
+    every code for E4M3; 0 and 8..126 for ExpCast, whose pre-codes below 8
+    become 0 (so 8 and 0 are neighbours)."""
     g = np.asarray(gpu_codes).astype(np.int64)
     r = np.asarray(ref_codes).astype(np.int64)
     diff = g != r
     per_row = diff.sum(axis=1)
+    if expcast:
+        assert not np.any((g > 0) & (g < 8)), f"{label}: an ExpCast code below 8 and not 0"
+        g, r = np.where(g == 0, 7, g), np.where(r == 0, 7, r)
     step = np.abs(g - r).max() if diff.any() else 0
     print(f"{label}: P codes differing {int(diff.sum())} of {diff.size} "
           f"({diff.mean():.2e}); per row max {int(per_row.max())} mean {per_row.mean():.2f}; "

@@ -102,10 +102,50 @@ def test_p_code_flips(name, stride, expcast, kmeans_kt, mma):
     for h in range(w.H):
         ref = oracle_head(q, k, v, 0, h, rows, expcast=expcast, kmeans_kt=kmeans_kt, trace=True)
         per_row = pcode_flips(codes[0, h, :len(rows), :w.S], ref["p_codes"],
-                              label=f"{name} {mma} expcast={expcast} h{h}")
+                              label=f"{name} {mma} expcast={expcast} h{h}", expcast=expcast)
         share.append(per_row.sum() / (len(rows) * w.S))
         assert np.all(codes[0, h, :len(rows), w.S:] == 0)      # padding keys
     assert max(share) <= (1e-3 if mma == "fp8" else 1e-5), share
+
+
+@pytest.mark.parametrize("mma", ["fp8", "bf16"])
+@pytest.mark.parametrize("expcast", [False, True])
+@pytest.mark.parametrize("case", ["rag129_d128", "rag300_d64", "rag1000_d128",
+                                  "large_positive", "large_negative"])
+def test_p_code_flips_on_stress_inputs(case, expcast, mma):
+    """The code-by-code comparison of test_p_code_flips on the inputs whose
+    FP8-product results are held to the relative-L2 bar only (x10 outlier
+    rows on ragged and small shapes, log2 scores far from 0): every code
+    that differs from the oracle's is one step away, a rounding boundary
+    crossed, so the larger max-abs and lse2 there come from those flips and
+    not from a wrong value.  Their share is printed; with the bf16 products
+    (float32-accurate scores) it stays below 1e-5."""
+    if case.startswith("rag"):
+        S, D = (int(t) for t in case[3:].split("_d"))
+        w = workloads.Workload("rag", 2, S, 3, D, 100 + S + D, "offsets",
+                               extra=dict(k_off=2.0, k_off_shared=False, v_off=1.0,
+                                          out_frac=0.01, out_mult=10.0))
+        q, k, v = workloads.generate(w)
+        smooth, stride = True, (1 if S <= 300 else 7)
+    else:
+        q, k, v, smooth = _extreme_inputs(case)
+        stride = 3
+    B, S, H, D = q.shape
+    plan = run_plan(q, k, v, smooth=smooth, expcast=expcast, mma=mma)
+    codes = plan.attn_pcodes(stride).cpu().numpy()
+    torch.cuda.synchronize()
+    rows = np.arange(0, S, stride)
+    share = []
+    for b in range(B):
+        for h in range(H):
+            ref = oracle_head(q, k, v, b, h, rows, smooth=smooth, expcast=expcast, trace=True)
+            per_row = pcode_flips(codes[b, h, :len(rows), :S], ref["p_codes"],
+                                  label=f"{case} {mma} expcast={expcast} b{b} h{h}",
+                                  expcast=expcast)
+            share.append(per_row.sum() / (len(rows) * S))
+            assert np.all(codes[b, h, :len(rows), S:] == 0)      # padding keys
+    if mma == "bf16":
+        assert max(share) <= 1e-5, share
 
 
 @pytest.mark.parametrize("mma", ["fp8", "bf16"])
@@ -252,15 +292,11 @@ def _bf16(x):
     return x.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("mma", ["fp8", "bf16"])
-@pytest.mark.parametrize("v_format", ["e4m3", "mxfp4"])
-@pytest.mark.parametrize("case", ["large_positive", "large_negative"])
-def test_extreme_score_ranges(case, v_format, mma):
-    """Rows whose running max lies far from 0 in log2 units (above 64, or
-    below -64 without smoothing): the bias 8 - m carried by the QK product's
-    accumulator and the shifts where the max grows keep the probabilities'
-    arguments in range.  Same oracle, same bars; the workloads stay in
-    [-8, 16]."""
+def _extreme_inputs(case):
+    """Q, K, V (bf16, [1, 700, 2, 128]) whose log2 scores lie far from 0:
+    large_positive ~ N(0, 57^2) (smoothed), large_negative every query
+    opposing the keys' shared direction (unsmoothed, since centring would
+    remove it).  Returns (q, k, v, smooth)."""
     g = torch.Generator().manual_seed(11)
     B, S, H, D = 1, 700, 2, 128
     q = torch.randn(B, S, H, D, generator=g)
@@ -274,7 +310,20 @@ def test_extreme_score_ranges(case, v_format, mma):
         k = u + 0.3 * k                  # keys share a direction ...
         q = -8.0 * u + 0.5 * q           # ... that every query opposes
         smooth = False                   # (centring would remove it)
-    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    return _bf16(q), _bf16(k), _bf16(v), smooth
+
+
+@pytest.mark.parametrize("mma", ["fp8", "bf16"])
+@pytest.mark.parametrize("v_format", ["e4m3", "mxfp4"])
+@pytest.mark.parametrize("case", ["large_positive", "large_negative"])
+def test_extreme_score_ranges(case, v_format, mma):
+    """Rows whose running max lies far from 0 in log2 units (above 64, or
+    below -64 without smoothing): the bias 8 - m carried by the QK product's
+    accumulator and the shifts where the max grows keep the probabilities'
+    arguments in range.  Same oracle, same bars; the workloads stay in
+    [-8, 16]."""
+    q, k, v, smooth = _extreme_inputs(case)
+    S, H = q.shape[1], q.shape[2]
     rows = np.arange(0, S, 3)
     for expcast in (False, True):
         plan = run_plan(q, k, v, smooth=smooth, expcast=expcast, v_format=v_format, mma=mma)
