@@ -6,9 +6,11 @@
 // operands -- FP8 v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 scales) or
 // bf16 v_mfma_f32_32x32x16_bf16 -- so the matrix core never waits on memory
 // or on a dependency, and records its s_memtime ticks (shader clock) around
-// the loop.  Flops per product: 2 * 32 * 32 * 64 (FP8), 2 * 32 * 32 * 16
-// (bf16).  The caller converts ticks and its own event time into the clock
-// and the rate.
+// the loop.  Each of the eight products has its own random A operand, so
+// consecutive products see different bytes.  Flops per product: 2 * 32 *
+// 32 * 64 (FP8), 2 * 32 * 32 * 16 (bf16).  The caller converts ticks and its
+// own event time into the clock and the rate.  mix_loop (below) runs the
+// attention kernel's two phase mixes for the clock each holds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,8 +28,8 @@ __device__ __forceinline__ uint32_t hash32(uint32_t x) {
   return x;
 }
 
-// Random E4M3 bytes of moderate size: exponent field kept in 4-10 and signs
-// random, so sums stay finite.
+// Four random E4M3 bytes of moderate size: random sign and mantissa, the
+// exponent field in 4-7 (magnitudes 1/8 to 15/8), so the sums stay finite.
 __device__ __forceinline__ uint32_t rand_e4m3x4(uint32_t x) {
   return (hash32(x) & 0x9F9F9F9Fu) | 0x20202020u;
 }
