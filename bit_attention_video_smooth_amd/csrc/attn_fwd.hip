@@ -280,6 +280,23 @@ __device__ __forceinline__ float tile_max(const v16f (&s)[4]) {
   return max_with_other_half(mx);
 }
 
+// The same tile max for the 4-bit probability tile, taken as the maxima gm
+// of the lane's two MX groups (sub-tiles 2 kk and 2 kk + 1 hold group kk's
+// 32 keys): the chain costs the same, and the groups' largest probabilities
+// are then 2^gm, with no second pass over the 64 values.
+__device__ __forceinline__ float tile_max_groups(const v16f (&s)[4], float (&gm)[2]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[2 * kk + u][r]);
+    gm[kk] = mx;
+  }
+  return max_with_other_half(__builtin_fmaxf(gm[0], gm[1]));
+}
+
 // E4M3 probability codes of 4 elements of one lane (the dword w of sub-tile
 // t of the B operand of PV): p8 = 2^x (x <= 8 up to rounding, so p8 <= 256
 // needs no clamp), rounded to nearest even by the FP8 conversion; the
@@ -323,7 +340,9 @@ __device__ __forceinline__ int expcast_codes4(const v16f& x, int w, float& ls) {
 // + 31 (registers r of sub-tiles 2 kk and 2 kk + 1 under the 4-bit row
 // mapping) form one MX group: e = the smallest exponent >= -127 with
 // max p8 <= 6 2^e -- from the float's bits: e = E - 2, plus 1 where the
-// mantissa exceeds 1.5 -- and the codes are E2M1(p8 2^-e), nearest with
+// mantissa exceeds 1.5; max p8 = 2^gm[kk], gm the group's largest x from
+// the tile max (2^x is monotone, so that is the largest of the p8) -- and
+// the codes are E2M1(p8 2^-e), nearest with
 // ties to the even code (the conversion divides by the power of two of the
 // scale operand's exponent field; a zero field acts as 2^-127).  A 4-bit
 // operand's lane half hh holds k positions 16 hh + (0..15) in nibbles 0-15
@@ -331,7 +350,7 @@ __device__ __forceinline__ int expcast_codes4(const v16f& x, int w, float& ls) {
 // position p with bits 4 and 5 of p swapped, so nibble n carries key
 // 64 kk + 32 hh + n: register n % 16 of sub-tile 2 kk + n / 16.
 template <int D, bool BF>
-__device__ __forceinline__ void p_tile_mxfp4(State<D, BF>& st, float& ls) {
+__device__ __forceinline__ void p_tile_mxfp4(State<D, BF>& st, float& ls, const float (&gm)[2]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -341,11 +360,7 @@ __device__ __forceinline__ void p_tile_mxfp4(State<D, BF>& st, float& ls) {
     }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, st.s[2 * kk + u][r]);
+    const float mx = __builtin_amdgcn_exp2f(gm[kk]);
     const uint32_t bits = __float_as_uint(mx);
     int e = static_cast<int>(bits >> 23) - 129 + ((bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
     e = mx > 0.0f ? (e < -127 ? -127 : e) : 0;
@@ -524,7 +539,9 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
   constexpr int DT = D / 32;
   if (j == c.nb - 1 && (c.S & (kBlock - 1)))
     mask_tile<PC == kPcMxfp4>(st.s, c.S - j * kBlock, c.hh);
-  const float xm = tile_max(st.s);   // max of s - m + 8 over the row's 128 keys
+  float gm[2];                      // 4-bit tile: the lane's MX group maxima of x
+  const float xm = PC == kPcMxfp4 ? tile_max_groups(st.s, gm)
+                                  : tile_max(st.s);   // max of s - m + 8 over the row's 128 keys
   // Tile 0 sets the reference (the bias was 0, so x = s); later tiles move
   // it where the row max grew.  tau = b - b' is the shift actually applied,
   // so x, O^T and l stay consistent with the new bias b'.
@@ -537,6 +554,11 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.s[t][r] -= tau;
+    if constexpr (PC == kPcMxfp4) {
+      // the same rounded subtraction of each group's largest x: still its max
+      gm[0] -= tau;
+      gm[1] -= tau;
+    }
     if (!first) {
       const float alpha = __builtin_amdgcn_exp2f(-tau);
 #pragma unroll
@@ -552,7 +574,7 @@ __device__ __forceinline__ void phase_valu(const int j, const Ctx<D, BF>& c, Sta
   float ls = 0.0f;
   int pk[16];
   if constexpr (PC == kPcMxfp4) {
-    p_tile_mxfp4(st, ls);
+    p_tile_mxfp4(st, ls, gm);
   } else {
 #pragma unroll
   for (int q = 0; q < 16; ++q)
